@@ -1,0 +1,259 @@
+"""Benchmark of the grouped top-4 W4A16 MoE FFN on one MI355X.
+
+Default workload (the metric's configuration): the 38-layer LFM2.5-24B-A2B
+MoE stack, batch-1 decode -- one step is one token through all 38 MoE layers
+(weightless pre-norm + BF16 residual between layers, fresh top-4 routing per
+layer and step), 64 steps timed warm after warm-up steps, as in the MXFP4
+card's benchmark protocol ("Benchmark decode separately from prefill":
+repeated 64-forward decode runs, first run excluded).  Inputs are seeded
+synthetic data already resident in HBM when timing starts; the weights of all
+38 x 64 experts (12.19 GB) stay resident and are read through the pointer
+tables.
+
+Prints one JSON line.  `value` is MoE-layer tokens/s (tokens through one MoE
+layer per second, i.e. 38 x the stack's tokens/s for the default workload).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+EPS = 1e-5
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=64)
+    p.add_argument("--warmup", type=int, default=64)
+    p.add_argument("--workload", default="c1", choices=["c1", "c0", "c2", "c2stack", "c3", "c4", "c4b32"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--calib", action="store_true",
+                   help="also run a 1 GiB stream read and a 256 MiB copy (counter calibration)")
+    p.add_argument("--graph", action="store_true", help="replay the timed steps from a HIP graph")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(expert-parallel sharding is a design note, not code). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from packed_bit_expert_amd import moe as M
+    from packed_bit_expert_amd import synth as S
+    from packed_bit_expert_amd.residency import ResidentExperts
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    shape = S.LFM24B
+    wname = {"c2stack": "c2"}.get(args.workload, args.workload)
+    w = S.WORKLOADS[wname]
+    stack = args.workload in ("c1", "c2stack")
+    T, E, K, H = w.tokens, shape.experts, shape.top_k, shape.hidden
+    # layers resident: the whole 38-layer stack for every workload, so single-
+    # layer workloads rotate over 38 layers and the reuse distance (762 MB+ per
+    # token) exceeds the 256 MB Infinity Cache.
+    L = shape.layers
+    t0 = time.time()
+    store = ResidentExperts(shape, w.fmt, L, device=dev).fill_synthetic()
+    print(f"[bench] {L} layers x {E} experts resident ({store.buf.numel() / 1e9:.2f} GB) "
+          f"in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    nsteps = args.warmup + args.steps
+    # per-step inputs (resident before timing)
+    if stack:
+        xs = torch.stack([torch.from_numpy(S.activations(w.family, 0, s, T, H).view(np.int16))
+                          for s in range(nsteps)]).view(torch.bfloat16).to(dev)
+        routes = [[S.routing(w, l, s) for l in range(L)] for s in range(nsteps)]
+        ids = torch.from_numpy(np.stack([[r[0] for r in rs] for rs in routes])).to(dev)  # [S][L][T][K]
+        rws = torch.from_numpy(np.stack([[r[1].view(np.int16) for r in rs] for rs in routes])).view(
+            torch.bfloat16).to(dev)
+    else:
+        xs = torch.stack([torch.from_numpy(S.activations(w.family, s % L, s, T, H).view(np.int16))
+                          for s in range(nsteps)]).view(torch.bfloat16).to(dev)
+        routes = [S.routing(w, s % L, s) for s in range(nsteps)]
+        ids = torch.from_numpy(np.stack([r[0] for r in routes])).to(dev)
+        rws = torch.from_numpy(np.stack([r[1].view(np.int16) for r in routes])).view(torch.bfloat16).to(dev)
+    out = torch.empty((nsteps, T, H), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    cfg = M.make_cfg(T, H, shape.inter, E, K, w.fmt, prenorm_eps=EPS, stream=stream)
+    if w.fmt == S.FMT_E4M3_G16:
+        cfg.tensor_scales = store.tscales[0].data_ptr()
+    ws = torch.zeros(M.moe_w4a16_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), ws.numel()
+
+    def step(s):
+        if stack:
+            ts = None if store.tscales is None else store.tscales
+            M.moe_w4a16_stack_forward(L, xs[s], ids[s], rws[s], store.wtab, store.stab, ts,
+                                      out[s], cfg)
+        else:
+            l = s % L
+            if store.tscales is not None:
+                cfg.tensor_scales = store.tscales[l].data_ptr()
+            M.moe_w4a16_forward(xs[s], ids[s], rws[s], store.wtab[l], store.stab[l], out[s], cfg)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for s in range(args.warmup, nsteps):
+                step(s)
+        torch.cuda.synchronize()
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for s in range(args.warmup, nsteps):
+            step(s)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    ms_step = ms / args.steps
+
+    # algorithmic bytes: each call reads its distinct selected experts' packed
+    # bytes once (+ activations in/out, negligible)
+    eb = shape.expert_bytes(w.fmt)
+    ids_h = ids[args.warmup:].cpu().numpy()
+    if stack:
+        distinct = sum(len(np.unique(ids_h[s, l])) for s in range(args.steps) for l in range(L))
+        layer_calls = args.steps * L
+    else:
+        distinct = sum(len(np.unique(ids_h[s])) for s in range(args.steps))
+        layer_calls = args.steps
+    alg_bytes = distinct * eb + layer_calls * 2 * T * H * 2
+    secs = ms / 1e3
+    achieved = alg_bytes / secs / 1e9
+    tok_layer_per_s = T * layer_calls / secs
+
+    # achievable HBM read bandwidth on this GPU (16-byte loads over 1 GiB)
+    if True:
+        buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        sink = torch.empty(4096, dtype=torch.int32, device=dev)
+        for _ in range(2):
+            M.moe_w4a16_stream_read(buf, buf.numel(), sink, stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            M.moe_w4a16_stream_read(buf, buf.numel(), sink, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        stream_gbps = 5 * buf.numel() / (e0.elapsed_time(e1) / 1e3) / 1e9
+        if args.calib:
+            src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            dst.copy_(src)
+            torch.cuda.synchronize()
+        del buf
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, shape, args.cpu_seconds)
+
+    launches = (1 if stack else 0)
+    res = {
+        "metric": "MoE-layer tokens/s & achieved HBM GB/s (% of peak), 24B-A2B shape, batch 1/32",
+        "value": tok_layer_per_s,
+        "unit": "tokens/s per MoE layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded E2M1 nibbles, E8M0 117..123 or E4M3 normal scales, x ~ N(0,1) BF16)",
+        "config": {
+            "workload": workload_name(args.workload),
+            "hidden": H, "inter": shape.inter, "experts": E, "top_k": K,
+            "layers_per_step": L if stack else 1, "tokens_per_step": T,
+            "weights": "E2M1 + E4M3/16 + FP32 tensor scale" if w.fmt else "E2M1 + E8M0/32",
+            "stack_tokens_per_s": T * args.steps / secs if stack else None,
+            "graph_replay": bool(args.graph),
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+            "kernel": "whole step (all MoE kernels of the step)",
+            "algorithmic_bytes_per_step": alg_bytes / args.steps,
+        },
+        "hbm_stream_read_GBps": stream_gbps,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def workload_name(k):
+    return {
+        "c1": "38-layer MoE stack, batch-1 decode (LFM2.5-24B-A2B, 2048/1536, 64 experts, top-4, E2M1+E8M0/32)",
+        "c0": "one MoE layer, 1 token (rotating over 38 resident layers)",
+        "c2": "concurrency-32 decode, Zipf(1.1) routing, one layer per call (rotating over 38 layers)",
+        "c2stack": "concurrency-32 decode through the 38-layer stack",
+        "c3": "prefill: S=64 chunks through one layer (rotating over 38 layers)",
+        "c4": "NVFP4-style E2M1+E4M3/16+FP32 tensor scale, batch 1",
+        "c4b32": "NVFP4-style E2M1+E4M3/16+FP32 tensor scale, batch 32",
+    }[k]
+
+
+def cpu_baseline(w, shape, target_s):
+    """The oracle as it stands on this host's cores, on a bounded sample: one
+    token (or one call of the workload's batch) through consecutive layers
+    until about `target_s` seconds of wall time have passed."""
+    import numpy as np
+
+    from oracle import oracle as O
+    from packed_bit_expert_amd import synth as S
+    threads = O.threads_available()
+    T = w.tokens
+    t0 = time.time()
+    layers = 0
+    tokens = 0
+    h = S.activations(w.family, 0, 10_000, T, shape.hidden)
+    gen_time = 0.0
+    while time.time() - t0 - gen_time < target_s and layers < shape.layers:
+        g0 = time.time()
+        ids, rw = S.routing(w, layers, 10_000)
+        nib = [None] * shape.experts
+        sc = [None] * shape.experts
+        for e in np.unique(ids):
+            nib[int(e)] = S.expert_nibbles(shape, w.fmt, layers, int(e))
+            sc[int(e)] = S.expert_scales(shape, w.fmt, layers, int(e))
+        ts = S.tensor_scales(shape, w.fmt, layers)
+        gen_time += time.time() - g0
+        out = O.moe_forward(h, ids, rw, nib, sc, hidden=shape.hidden, inter=shape.inter,
+                            num_experts=shape.experts, fmt=w.fmt, tensor_scales=ts,
+                            residual=h if w.chained else None, prenorm=w.chained, eps=EPS)
+        h = out if w.chained else h
+        layers += 1
+        tokens += T
+    wall = time.time() - t0 - gen_time
+    return {"value": tokens / wall, "unit": "tokens/s per MoE layer", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{layers} layer calls of {T} token(s) ({w.name} inputs), fp64 scalar oracle, "
+                      f"{threads} OpenMP threads, {wall:.1f} s (input generation excluded)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,237 @@
+/*
+ * moe_w4a16.h -- C ABI of the MI355X (gfx950) grouped top-k W4A16 MoE FFN.
+ *
+ * The operation ("LFM2.5-24B-A2B -- Packed MXFP4 Inference", sections "Model
+ * and quantization" and "What was optimized / Grouped top-4 expert
+ * execution"): for every token t and routing slot j with expert e = ids[t][j],
+ *
+ *     u      = x[t], or the weightless RMS pre-norm of x[t] (MOE_FLAG_PRENORM)
+ *     g      = bf16(Wg_e u)          grouped gate GEMV, FP32 accumulation
+ *     v      = bf16(Wu_e u)          grouped up GEMV
+ *     h      = bf16(silu(g) * v)     activation and multiplication
+ *     y_j    = bf16(Wd_e h)          grouped down GEMV
+ *     out[t] = sequential BF16 combine over slots 0..k-1 of bf16(w[t][j] * y_j),
+ *              each product and each add rounded to BF16 separately, starting
+ *              from +0; then, with a residual, out = bf16(residual + out).
+ *
+ * Expert weights stay packed: E2M1 FP4 values two per byte with one E8M0
+ * scale per 32 values (MOE_SCALE_E8M0_G32, the MXFP4 card's format), or one
+ * E4M3FN scale per 16 values plus an FP32 per-expert tensor scale shared by
+ * gate and up and a second one for down (MOE_SCALE_E4M3_G16, the NVFP4
+ * weight-only variant of "primitive-ai/LFM2.5-24B-A2B-NVFP4A16", section
+ * "What's quantized to what").  Activations and outputs are BF16.
+ *
+ * Packed layout (the only layout; one expert):
+ *   packed_weights[e] -> gate [I][H/2] | up [I][H/2] | down [H][I/2]  bytes
+ *   scales[e]         -> gate [I][H/G] | up [I][H/G] | down [H][I/G]  bytes
+ * Matrices are [out][in], row-major.  Byte i of a row holds element 2i in bits
+ * 0..3 and element 2i+1 in bits 4..7.  The scale of element (n, k) is byte
+ * k / G of row n (G = 32 for E8M0, 16 for E4M3FN).  The two bases may point
+ * into one contiguous buffer per expert (nibbles then scales: the "expert
+ * triplet as one contiguous byte buffer" of the MXFP4 card's "Bounded pinned
+ * RAM expert cache").  Every base must be 16-byte aligned (256 recommended).
+ *
+ * Pointer tables.  packed_weights and scales are DEVICE arrays of E device
+ * pointers, built once per layer by the caller and kept ("Direct reads from
+ * GPU-resident weights": resident experts are read in place through
+ * persistent device pointer tables, with no staging copy).  Kernels read the
+ * tables and expert_ids on the device, so both may change between calls or
+ * between replays of a captured HIP graph without re-capture ("GPU routing
+ * inside resident-layer graphs": selection is recomputed on every replay and
+ * ids are never copied back to the CPU).  The library never reads device data
+ * on the host and never synchronises in a forward call.
+ *
+ * Ownership.  The caller owns every buffer: inputs, tables, weights, outputs
+ * and the workspace.  The library allocates and frees nothing in the calls
+ * below and keeps no device state between calls.  All device work is
+ * enqueued on cfg->stream (a hipStream_t; NULL = the default stream) and the
+ * call returns without waiting.  Calls that share a workspace must be
+ * ordered (same stream, or synchronised); distinct workspaces and streams
+ * may run concurrently.
+ *
+ * Errors.  Every int-returning function returns MOE_OK (0) or a negative
+ * MOE_ERR_* code.  Argument checks read only host values (cfg fields and
+ * pointer values), run before anything is enqueued, and leave nothing
+ * enqueued on failure.  moe_w4a16_last_error() gives a message for the
+ * calling thread's last failure.  Invalid expert ids or misaligned expert
+ * bases inside the device tables cannot be seen on the host: they are
+ * undefined behaviour unless MOE_FLAG_CHECK_IDS is set, in which case the
+ * kernels skip the bad slot, write an error word into the workspace and
+ * moe_w4a16_device_status() reports it.
+ */
+#ifndef MOE_W4A16_H
+#define MOE_W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_W4A16_ABI_VERSION 1
+
+/* return codes */
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1)          /* null pointer, bad enum, T < 0, aliasing, ... */
+#define MOE_ERR_UNSUPPORTED_SHAPE (-2)    /* hidden / inter / top_k / experts not supported */
+#define MOE_ERR_MISALIGNED (-3)           /* a pointer breaks its documented alignment */
+#define MOE_ERR_WORKSPACE_TOO_SMALL (-4)  /* workspace_bytes < moe_w4a16_workspace_bytes() */
+#define MOE_ERR_ABI_MISMATCH (-5)         /* cfg->abi_version != MOE_W4A16_ABI_VERSION */
+#define MOE_ERR_HIP (-6)                  /* a HIP runtime call failed (text in last_error) */
+#define MOE_ERR_DEVICE_CHECK (-7)         /* a device-side check (MOE_FLAG_CHECK_IDS) failed */
+
+/* scale formats */
+#define MOE_SCALE_E8M0_G32 0  /* E8M0 2^(e-127), one per 32 values along K (MXFP4) */
+#define MOE_SCALE_E4M3_G16 1  /* E4M3FN, one per 16 values, times an FP32 tensor scale */
+
+/* flags */
+#define MOE_FLAG_PRENORM (1u << 0)        /* u = bf16(x * rsqrt(mean(x^2) + prenorm_eps)) */
+#define MOE_FLAG_FORCE_DECODE (1u << 1)   /* use the per-token GEMV path for any T */
+#define MOE_FLAG_FORCE_BATCHED (1u << 2)  /* use the sorted MFMA path even at T = 1 */
+#define MOE_FLAG_CHECK_IDS (1u << 3)      /* device-side id / alignment checks */
+
+typedef struct moe_w4a16_cfg {
+  int32_t abi_version;         /* MOE_W4A16_ABI_VERSION */
+  int32_t num_tokens;          /* T >= 0; T = 0 is a no-op */
+  int32_t hidden;              /* H; see moe_w4a16_shape_supported() */
+  int32_t inter;               /* I, the expert intermediate size */
+  int32_t num_experts;         /* E, 1..1024 */
+  int32_t top_k;               /* k, 1..8 */
+  int32_t scale_fmt;           /* MOE_SCALE_* */
+  uint32_t flags;              /* MOE_FLAG_* */
+  const float* tensor_scales;  /* device [E][2] FP32 {gate_up, down}: required for
+                                  E4M3, must be NULL for E8M0 */
+  const void* residual;        /* optional device BF16 [T][H]; may alias x */
+  float prenorm_eps;           /* used with MOE_FLAG_PRENORM */
+  int32_t reserved0;
+  void* workspace;             /* device, 256-byte aligned, see below */
+  size_t workspace_bytes;
+  void* stream;                /* hipStream_t or NULL */
+} moe_w4a16_cfg;
+
+/* Debug dumps: device BF16 buffers, each optional (NULL = not written). */
+typedef struct moe_w4a16_dump {
+  void* u;  /* [T][H]     activation fed to gate/up (after the pre-norm) */
+  void* g;  /* [T][k][I]  gate outputs */
+  void* v;  /* [T][k][I]  up outputs */
+  void* h;  /* [T][k][I]  silu(g) * v */
+  void* y;  /* [T][k][H]  down outputs, before the combine */
+} moe_w4a16_dump;
+
+/* MOE_W4A16_ABI_VERSION of the loaded library. */
+int moe_w4a16_abi_version(void);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* moe_w4a16_last_error(void);
+
+/* 1 if (hidden, inter) is supported for the given token count and flags
+ * (both must be multiples of 256 and at most 16384; the one-launch decode
+ * path used at T = 1 is compiled for hidden/inter pairs (2048, 1536),
+ * (1024, 768) and (512, 256); other pairs fall back to the batched path). */
+int moe_w4a16_shape_supported(int32_t hidden, int32_t inter);
+
+/* Workspace bytes needed by moe_w4a16_forward / _forward_debug /
+ * _stack_forward with this cfg (it depends on T, H, I, E, k and flags).
+ * Returns 0 for an invalid cfg. */
+size_t moe_w4a16_workspace_bytes(const moe_w4a16_cfg* cfg);
+
+/* Zero-fill a workspace on `stream` (a kernel, not a memset node, so it can
+ * be captured).  A workspace must be zeroed once before its first use; every
+ * forward call leaves its control words zeroed again on exit. */
+int moe_w4a16_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/*
+ * One MoE layer: out = combine(experts(x)) (+ residual), all in BF16.
+ *   x          device BF16 [T][H], 16-byte aligned
+ *   expert_ids device int32 [T][k]; duplicates within a token are allowed
+ *              (each slot is computed on its own)
+ *   route_w    device BF16 [T][k] routing coefficients
+ *   packed_weights, scales   device tables [E] of device pointers (layout above)
+ *   out        device BF16 [T][H], 16-byte aligned, must not overlap x
+ * T = 1 uses the one-launch decode kernel; T > 1 uses the sorted batched
+ * path (device-side stable sort of the (token, slot) pairs by expert, then
+ * grouped BF16-MFMA GEMMs on LDS-dequantised tiles, then the combine).
+ */
+int moe_w4a16_forward(const void* x, const int32_t* expert_ids, const void* route_w,
+                      const void* const* packed_weights, const void* const* scales,
+                      void* out, const moe_w4a16_cfg* cfg);
+
+/* moe_w4a16_forward that also writes the intermediates named in `dump`
+ * (device pointers; dump may be NULL).  Same kernels, same results. */
+int moe_w4a16_forward_debug(const void* x, const int32_t* expert_ids, const void* route_w,
+                            const void* const* packed_weights, const void* const* scales,
+                            void* out, const moe_w4a16_cfg* cfg, const moe_w4a16_dump* dump);
+
+/*
+ * L chained MoE layers (the 38-layer MoE stack of LFM2.5-24B-A2B, "Model and
+ * quantization": 40 layers of which 38 are MoE), batch T:
+ *     h_0 = x;  h_{l+1} = bf16(h_l + MoE_l(prenorm(h_l)));  out = h_L
+ * with the weightless pre-norm always applied (cfg->prenorm_eps) and the
+ * residual always the layer input (cfg->residual and MOE_FLAG_PRENORM are
+ * ignored).  Layer l uses expert_ids + l*T*k, route_w + l*T*k (BF16),
+ * packed_weights + l*E, scales + l*E and, for E4M3, tensor_scales + l*E*2.
+ *   x, out      device BF16 [T][H]; out must not overlap x
+ *   expert_ids  device int32 [L][T][k]; route_w device BF16 [L][T][k]
+ *   packed_weights, scales   device tables [L][E]
+ *   tensor_scales            device FP32 [L][E][2] (E4M3) or NULL (E8M0)
+ * At T = 1 the whole stack is one kernel launch; otherwise one batched
+ * sequence per layer.
+ */
+int moe_w4a16_stack_forward(int32_t num_layers, const void* x, const int32_t* expert_ids,
+                            const void* route_w, const void* const* packed_weights,
+                            const void* const* scales, const float* tensor_scales, void* out,
+                            const moe_w4a16_cfg* cfg);
+
+/*
+ * Test hook: dequantise one packed [rows][cols] matrix to BF16 with the same
+ * device decoders the GEMM kernels use.  E2M1 * E8M0 and E2M1 * E4M3FN are
+ * exact in BF16, so the result is the exact dequantised value ("Model and
+ * quantization": packed E2M1, E8M0 scale per 32 values).  No tensor scale is
+ * applied.  nibbles [rows][cols/2], scales [rows][cols/G], out BF16
+ * [rows][cols]; cols a multiple of 32, all device pointers.
+ */
+int moe_w4a16_dequant(const void* nibbles, const void* scales, int32_t rows, int32_t cols,
+                      int32_t scale_fmt, void* out, void* stream);
+
+/*
+ * The order-preserving combine on its own ("Grouped top-4 expert execution":
+ * the fused routing-weighted combination keeps the sequential BF16
+ * multiply/add rounding), with the same device function the forward kernels
+ * use: out[t][m] = fold over j = 0..k-1 of acc = bf16(acc + bf16(w[t][j] *
+ * y[t][j][m])) from acc = +0, then bf16(residual[t][m] + acc) if residual.
+ *   y device BF16 [T][k][H]; route_w BF16 [T][k]; residual BF16 [T][H] or NULL;
+ *   out BF16 [T][H].
+ */
+int moe_w4a16_combine(const void* y, const void* route_w, const void* residual, void* out,
+                      int32_t num_tokens, int32_t top_k, int32_t hidden, void* stream);
+
+/*
+ * The batched path's grouping step on its own: a stable counting sort of the
+ * T*k (token, slot) pairs by expert id, on the device ("BatchedMetalSwitchGLU
+ * serves S=64 by sorting (token, expert) pairs", visible-cx/LFM2.5-8B-A1B-CoreAI,
+ * "Provenance").  counts [E], offsets [E+1] (offsets[0] = 0), perm [T*k] with
+ * perm[i] = t*k + j, pairs of one expert contiguous and in (t, j) order.
+ * All device int32 buffers; nothing is read back.  Ids outside [0, E) are
+ * undefined behaviour (they are counted in no bin).
+ */
+int moe_w4a16_sort_pairs(const int32_t* expert_ids, int32_t num_tokens, int32_t top_k,
+                         int32_t num_experts, int32_t* counts, int32_t* offsets, int32_t* perm,
+                         void* stream);
+
+/* Reads (and clears) the device error word of a workspace; synchronises
+ * `stream`.  *host_code = 0 if no device check failed, else a bitmask:
+ * 1 = expert id out of range, 2 = misaligned expert base.  Returns
+ * MOE_ERR_DEVICE_CHECK when *host_code != 0. */
+int moe_w4a16_device_status(void* workspace, int32_t* host_code, void* stream);
+
+/* Measurement helper: stream-read `bytes` (multiple of 16) from device
+ * memory `src` with 16-byte loads over the whole GPU and write one word per
+ * workgroup to `sink` (device, 4 * 4096 bytes), to measure the achievable
+ * HBM read bandwidth next to the kernels above. */
+int moe_w4a16_stream_read(const void* src, size_t bytes, void* sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_W4A16_H */

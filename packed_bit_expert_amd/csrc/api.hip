@@ -1,0 +1,372 @@
+// C ABI of the W4A16 MoE library: argument checks, workspace layout, path
+// selection.  Every check reads host values only (cfg fields and pointer
+// values) and runs before anything is enqueued.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return MOE_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na && nb && x < y + nb && y < x + na;
+}
+
+// Workspace regions (offsets from the base, each 256-byte aligned).
+struct Layout {
+  size_t meta, perm, hbuf, ybuf, ping, total;
+};
+
+Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
+  Layout L;
+  size_t off = kCtrlBytes;
+  L.meta = off;  // counts[E], offsets[E+1], active[E], nactive
+  off += align256((size_t)(3 * E + 2) * 4);
+  L.perm = off;
+  off += align256((size_t)(T * K) * 4);
+  L.hbuf = off;
+  off += align256((size_t)(T * K * I) * 2);
+  L.ybuf = off;
+  off += align256((size_t)(T * K * H) * 2);
+  L.ping = off;
+  off += align256((size_t)(T * H) * 2);
+  L.total = off;
+  return L;
+}
+
+int check_shape(const moe_w4a16_cfg* c) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->abi_version != MOE_W4A16_ABI_VERSION)
+    return fail(MOE_ERR_ABI_MISMATCH, "cfg->abi_version %d, library %d", c->abi_version,
+                MOE_W4A16_ABI_VERSION);
+  if (c->num_tokens < 0) return fail(MOE_ERR_INVALID_ARG, "num_tokens %d < 0", c->num_tokens);
+  if (c->num_experts < 1 || c->num_experts > 1024)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "num_experts %d outside 1..1024", c->num_experts);
+  if (c->top_k < 1 || c->top_k > 8)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "top_k %d outside 1..8", c->top_k);
+  if (c->scale_fmt != MOE_SCALE_E8M0_G32 && c->scale_fmt != MOE_SCALE_E4M3_G16)
+    return fail(MOE_ERR_INVALID_ARG, "scale_fmt %d unknown", c->scale_fmt);
+  if (!moe_w4a16_shape_supported(c->hidden, c->inter))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "hidden %d / inter %d not supported", c->hidden,
+                c->inter);
+  const uint32_t known = MOE_FLAG_PRENORM | MOE_FLAG_FORCE_DECODE | MOE_FLAG_FORCE_BATCHED |
+                         MOE_FLAG_CHECK_IDS;
+  if (c->flags & ~known) return fail(MOE_ERR_INVALID_ARG, "unknown flag bits 0x%x", c->flags);
+  if ((c->flags & MOE_FLAG_FORCE_DECODE) && (c->flags & MOE_FLAG_FORCE_BATCHED))
+    return fail(MOE_ERR_INVALID_ARG, "FORCE_DECODE and FORCE_BATCHED together");
+  if ((c->flags & MOE_FLAG_FORCE_DECODE) && !decode_supported(c->hidden, c->inter))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "no decode kernel for hidden %d / inter %d",
+                c->hidden, c->inter);
+  if (c->scale_fmt == MOE_SCALE_E4M3_G16 && !c->tensor_scales)
+    return fail(MOE_ERR_INVALID_ARG, "E4M3 scales need tensor_scales");
+  if (c->scale_fmt == MOE_SCALE_E8M0_G32 && c->tensor_scales)
+    return fail(MOE_ERR_INVALID_ARG, "tensor_scales must be NULL for E8M0 scales");
+  if ((c->flags & MOE_FLAG_PRENORM) && !(c->prenorm_eps >= 0.f))
+    return fail(MOE_ERR_INVALID_ARG, "prenorm_eps must be >= 0");
+  return MOE_OK;
+}
+
+bool use_decode(const moe_w4a16_cfg* c) {
+  if (c->flags & MOE_FLAG_FORCE_BATCHED) return false;
+  if (c->flags & MOE_FLAG_FORCE_DECODE) return true;
+  return c->num_tokens == 1 && decode_supported(c->hidden, c->inter);
+}
+
+struct Call {
+  const void* x;
+  const int32_t* ids;
+  const void* rw;
+  const void* const* wtab;
+  const void* const* stab;
+  const float* tsc;
+  const void* residual;
+  void* out;
+  const moe_w4a16_dump* dump;
+};
+
+int check_call(const moe_w4a16_cfg* c, const Call& k) {
+  int rc = check_shape(c);
+  if (rc) return rc;
+  const size_t T = (size_t)c->num_tokens;
+  if (T == 0) return MOE_OK;
+  if (!k.x || !k.ids || !k.rw || !k.wtab || !k.stab || !k.out)
+    return fail(MOE_ERR_INVALID_ARG, "x, expert_ids, route_w, tables and out must be non-NULL");
+  if (!c->workspace) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(k.x, 16) || !aligned(k.out, 16) || (k.residual && !aligned(k.residual, 16)))
+    return fail(MOE_ERR_MISALIGNED, "x, out and residual must be 16-byte aligned");
+  if (!aligned(k.ids, 4) || !aligned(k.rw, 2) || !aligned(k.wtab, 8) || !aligned(k.stab, 8))
+    return fail(MOE_ERR_MISALIGNED, "ids, route_w or a pointer table is misaligned");
+  if (k.tsc && !aligned(k.tsc, 4)) return fail(MOE_ERR_MISALIGNED, "tensor_scales misaligned");
+  if (!aligned(c->workspace, 256)) return fail(MOE_ERR_MISALIGNED, "workspace not 256-byte aligned");
+  const size_t act = T * (size_t)c->hidden * 2;
+  if (overlap(k.x, act, k.out, act)) return fail(MOE_ERR_INVALID_ARG, "out overlaps x");
+  if (k.residual && overlap(k.residual, act, k.out, act) && k.residual != k.out)
+    return fail(MOE_ERR_INVALID_ARG, "out partially overlaps residual");
+  const size_t need = moe_w4a16_workspace_bytes(c);
+  if (c->workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", c->workspace_bytes,
+                need);
+  if (k.dump) {
+    const void* d[5] = {k.dump->u, k.dump->g, k.dump->v, k.dump->h, k.dump->y};
+    for (int i = 0; i < 5; ++i)
+      if (d[i] && !aligned(d[i], 2)) return fail(MOE_ERR_MISALIGNED, "dump buffer misaligned");
+  }
+  return MOE_OK;
+}
+
+int run_layer(const moe_w4a16_cfg* c, const Call& k) {
+  const int T = c->num_tokens;
+  if (T == 0) return ok();
+  hipStream_t s = (hipStream_t)c->stream;
+  const Layout L = layout(T, c->hidden, c->inter, c->num_experts, c->top_k);
+  uint8_t* ws = (uint8_t*)c->workspace;
+  int* err = &((Ctrl*)ws)->err;
+  const moe_w4a16_dump* d = k.dump;
+  hipError_t e;
+  if (use_decode(c)) {
+    DecodeArgs a;
+    a.x = (const uint16_t*)k.x;
+    a.ids = k.ids;
+    a.rw = (const uint16_t*)k.rw;
+    a.wtab = (const uint8_t* const*)k.wtab;
+    a.stab = (const uint8_t* const*)k.stab;
+    a.tsc = k.tsc;
+    a.residual = (const uint16_t*)k.residual;
+    a.out = (uint16_t*)k.out;
+    a.hbuf = (uint16_t*)(ws + L.hbuf);
+    a.du = d ? (uint16_t*)d->u : nullptr;
+    a.dg = d ? (uint16_t*)d->g : nullptr;
+    a.dv = d ? (uint16_t*)d->v : nullptr;
+    a.dh = d ? (uint16_t*)d->h : nullptr;
+    a.dy = d ? (uint16_t*)d->y : nullptr;
+    a.err = err;
+    a.T = T;
+    a.H = c->hidden;
+    a.I = c->inter;
+    a.K = c->top_k;
+    a.E = c->num_experts;
+    a.flags = c->flags;
+    a.eps = c->prenorm_eps;
+    e = launch_decode(a, c->scale_fmt, s);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return ok();
+  }
+  BatchedArgs a;
+  a.x = (const uint16_t*)k.x;
+  a.ids = k.ids;
+  a.rw = (const uint16_t*)k.rw;
+  a.wtab = (const uint8_t* const*)k.wtab;
+  a.stab = (const uint8_t* const*)k.stab;
+  a.tsc = k.tsc;
+  a.residual = (const uint16_t*)k.residual;
+  a.out = (uint16_t*)k.out;
+  int32_t* meta = (int32_t*)(ws + L.meta);
+  a.counts = meta;
+  a.offsets = meta + c->num_experts;
+  a.active = meta + 2 * c->num_experts + 1;
+  a.nactive = meta + 3 * c->num_experts + 1;
+  a.perm = (int32_t*)(ws + L.perm);
+  a.hbuf = (uint16_t*)(ws + L.hbuf);
+  a.ybuf = (uint16_t*)(ws + L.ybuf);
+  a.du = d ? (uint16_t*)d->u : nullptr;
+  a.dg = d ? (uint16_t*)d->g : nullptr;
+  a.dv = d ? (uint16_t*)d->v : nullptr;
+  a.dh = d ? (uint16_t*)d->h : nullptr;
+  a.dy = d ? (uint16_t*)d->y : nullptr;
+  a.err = err;
+  a.T = T;
+  a.H = c->hidden;
+  a.I = c->inter;
+  a.K = c->top_k;
+  a.E = c->num_experts;
+  a.mc = batched_chunk_tokens(c->hidden, c->inter);
+  a.flags = c->flags;
+  a.eps = c->prenorm_eps;
+  if (c->flags & MOE_FLAG_CHECK_IDS) {
+    // pairs that a device check drops must still combine as y = 0
+    e = launch_zero(a.ybuf, (size_t)T * c->top_k * c->hidden * 2, s);
+    if (e != hipSuccess) return hip_fail(e, "workspace clear");
+    if (d && d->y) {
+      e = launch_zero(d->y, (size_t)T * c->top_k * c->hidden * 2, s);
+      if (e != hipSuccess) return hip_fail(e, "dump clear");
+    }
+  }
+  e = launch_batched(a, c->scale_fmt, s);
+  if (e != hipSuccess) return hip_fail(e, "batched launch");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_w4a16_abi_version(void) { return MOE_W4A16_ABI_VERSION; }
+
+const char* moe_w4a16_last_error(void) { return g_err; }
+
+int moe_w4a16_shape_supported(int32_t hidden, int32_t inter) {
+  return batched_supported(hidden, inter) ? 1 : 0;
+}
+
+size_t moe_w4a16_workspace_bytes(const moe_w4a16_cfg* cfg) {
+  if (check_shape(cfg) != MOE_OK) return 0;
+  return layout(cfg->num_tokens, cfg->hidden, cfg->inter, cfg->num_experts, cfg->top_k).total;
+}
+
+int moe_w4a16_workspace_init(void* workspace, size_t bytes, void* stream) {
+  if (!workspace) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+  hipError_t e = launch_zero(workspace, bytes, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "workspace init");
+}
+
+int moe_w4a16_forward_debug(const void* x, const int32_t* expert_ids, const void* route_w,
+                            const void* const* packed_weights, const void* const* scales,
+                            void* out, const moe_w4a16_cfg* cfg, const moe_w4a16_dump* dump) {
+  Call k{x, expert_ids, route_w, packed_weights, scales, cfg ? cfg->tensor_scales : nullptr,
+         cfg ? cfg->residual : nullptr, out, dump};
+  int rc = check_call(cfg, k);
+  if (rc) return rc;
+  return run_layer(cfg, k);
+}
+
+int moe_w4a16_forward(const void* x, const int32_t* expert_ids, const void* route_w,
+                      const void* const* packed_weights, const void* const* scales, void* out,
+                      const moe_w4a16_cfg* cfg) {
+  return moe_w4a16_forward_debug(x, expert_ids, route_w, packed_weights, scales, out, cfg,
+                                 nullptr);
+}
+
+int moe_w4a16_stack_forward(int32_t num_layers, const void* x, const int32_t* expert_ids,
+                            const void* route_w, const void* const* packed_weights,
+                            const void* const* scales, const float* tensor_scales, void* out,
+                            const moe_w4a16_cfg* cfg) {
+  if (num_layers < 1) return fail(MOE_ERR_INVALID_ARG, "num_layers %d < 1", num_layers);
+  if (!cfg) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+  moe_w4a16_cfg lc = *cfg;
+  lc.flags |= MOE_FLAG_PRENORM;
+  lc.tensor_scales = tensor_scales;
+  lc.residual = x;
+  Call k{x, expert_ids, route_w, packed_weights, scales, tensor_scales, x, out, nullptr};
+  int rc = check_call(&lc, k);
+  if (rc) return rc;
+  const int64_t T = lc.num_tokens, K = lc.top_k, E = lc.num_experts;
+  if (T == 0) return ok();
+  const Layout L = layout(T, lc.hidden, lc.inter, E, K);
+  void* ping = (uint8_t*)lc.workspace + L.ping;
+  const void* src = x;
+  for (int l = 0; l < num_layers; ++l) {
+    void* dst = ((num_layers - 1 - l) % 2 == 0) ? out : ping;
+    lc.residual = src;
+    lc.tensor_scales = tensor_scales ? tensor_scales + (size_t)l * E * 2 : nullptr;
+    Call kl{src, expert_ids + (size_t)l * T * K, (const uint16_t*)route_w + (size_t)l * T * K,
+            packed_weights + (size_t)l * E, scales + (size_t)l * E, lc.tensor_scales, src, dst,
+            nullptr};
+    rc = run_layer(&lc, kl);
+    if (rc) return rc;
+    src = dst;
+  }
+  return ok();
+}
+
+int moe_w4a16_dequant(const void* nibbles, const void* scales, int32_t rows, int32_t cols,
+                      int32_t scale_fmt, void* out, void* stream) {
+  if (!nibbles || !scales || !out) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  if (rows < 0 || cols <= 0 || cols % 32)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "rows %d / cols %d (cols must be a multiple of 32)",
+                rows, cols);
+  if (scale_fmt != MOE_SCALE_E8M0_G32 && scale_fmt != MOE_SCALE_E4M3_G16)
+    return fail(MOE_ERR_INVALID_ARG, "scale_fmt %d unknown", scale_fmt);
+  if (!aligned(nibbles, 16) || !aligned(out, 16) || !aligned(scales, 2))
+    return fail(MOE_ERR_MISALIGNED, "nibbles and out need 16-byte alignment");
+  hipError_t e = launch_dequant((const uint8_t*)nibbles, (const uint8_t*)scales, rows, cols,
+                                scale_fmt, (uint16_t*)out, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "dequant launch");
+}
+
+int moe_w4a16_combine(const void* y, const void* route_w, const void* residual, void* out,
+                      int32_t num_tokens, int32_t top_k, int32_t hidden, void* stream) {
+  if (num_tokens < 0 || top_k < 1 || top_k > 8 || hidden <= 0 || hidden % 8)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "T %d, k %d, H %d (H must be a multiple of 8)",
+                num_tokens, top_k, hidden);
+  if (num_tokens == 0) return ok();
+  if (!y || !route_w || !out) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned(y, 16) || !aligned(out, 16) || (residual && !aligned(residual, 16)) ||
+      !aligned(route_w, 2))
+    return fail(MOE_ERR_MISALIGNED, "y, out and residual need 16-byte alignment");
+  hipError_t e = launch_combine((const uint16_t*)y, (const uint16_t*)route_w,
+                                (const uint16_t*)residual, (uint16_t*)out, num_tokens, top_k,
+                                hidden, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "combine launch");
+}
+
+int moe_w4a16_sort_pairs(const int32_t* expert_ids, int32_t num_tokens, int32_t top_k,
+                         int32_t num_experts, int32_t* counts, int32_t* offsets, int32_t* perm,
+                         void* stream) {
+  if (num_tokens < 0 || top_k < 1 || top_k > 8 || num_experts < 1 || num_experts > 1024)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "T %d, k %d, E %d", num_tokens, top_k, num_experts);
+  if (!expert_ids || !counts || !offsets || (num_tokens > 0 && !perm))
+    return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned(expert_ids, 4) || !aligned(counts, 4) || !aligned(offsets, 4) ||
+      !aligned(perm, 4))
+    return fail(MOE_ERR_MISALIGNED, "int32 buffers need 4-byte alignment");
+  // the hook writes counts, offsets and perm only (no active-expert list)
+  hipError_t e = launch_sort(expert_ids, num_tokens * top_k, num_experts, counts, offsets, perm,
+                             nullptr, nullptr, nullptr, 0, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "sort launch");
+}
+
+int moe_w4a16_device_status(void* workspace, int32_t* host_code, void* stream) {
+  if (!workspace || !host_code) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  hipStream_t s = (hipStream_t)stream;
+  int v = 0;
+  hipError_t e = hipMemcpyAsync(&v, &((Ctrl*)workspace)->err, sizeof(int), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "device status read");
+  if (v) {
+    const int zero = 0;
+    e = hipMemcpyAsync(&((Ctrl*)workspace)->err, &zero, sizeof(int), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "device status clear");
+  }
+  *host_code = v;
+  if (v) return fail(MOE_ERR_DEVICE_CHECK, "device check failed: code %d", v);
+  return ok();
+}
+
+int moe_w4a16_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+  if (!src || !sink) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  if (bytes % 16 || !aligned(src, 16) || !aligned(sink, 4))
+    return fail(MOE_ERR_MISALIGNED, "src needs 16-byte alignment and a multiple of 16 bytes");
+  hipError_t e = launch_stream_read(src, bytes, (uint32_t*)sink, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "stream read launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Kernel launchers of the W4A16 MoE library (host side of the HIP kernels).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Arguments of the per-token GEMV path (decode).  All pointers are device
+// pointers; the dump pointers may be null.
+struct DecodeArgs {
+  const uint16_t* x;          // [T][H] BF16
+  const int32_t* ids;         // [T][K]
+  const uint16_t* rw;         // [T][K] BF16 routing coefficients
+  const uint8_t* const* wtab; // [E] packed-nibble bases
+  const uint8_t* const* stab; // [E] scale bases
+  const float* tsc;           // [E][2] FP32 tensor scales (E4M3) or null
+  const uint16_t* residual;   // [T][H] or null
+  uint16_t* out;              // [T][H]
+  uint16_t* hbuf;             // [T][K][I] workspace
+  uint16_t *du, *dg, *dv, *dh, *dy;
+  int* err;                   // device error word
+  int T, H, I, K, E;
+  uint32_t flags;
+  float eps;
+};
+
+// Arguments of the sorted batched path.
+struct BatchedArgs {
+  const uint16_t* x;
+  const int32_t* ids;
+  const uint16_t* rw;
+  const uint8_t* const* wtab;
+  const uint8_t* const* stab;
+  const float* tsc;
+  const uint16_t* residual;
+  uint16_t* out;
+  int32_t* counts;    // [E]
+  int32_t* offsets;   // [E + 1]
+  int32_t* active;    // [E] experts with at least one pair, in id order
+  int32_t* nactive;   // [1]
+  int32_t* perm;      // [T * K]
+  uint16_t* hbuf;     // [T * K][I]
+  uint16_t* ybuf;     // [T * K][H]
+  uint16_t *du, *dg, *dv, *dh, *dy;
+  int* err;
+  int T, H, I, K, E;
+  int mc;             // tokens per LDS chunk (16 or 32)
+  uint32_t flags;
+  float eps;
+};
+
+bool decode_supported(int H, int I);
+bool batched_supported(int H, int I);
+int batched_chunk_tokens(int H, int I);
+
+hipError_t launch_decode(const DecodeArgs& a, int fmt, hipStream_t s);
+hipError_t launch_batched(const BatchedArgs& a, int fmt, hipStream_t s);
+hipError_t launch_sort(const int32_t* ids, int npairs, int E, int32_t* counts, int32_t* offsets,
+                       int32_t* perm, int32_t* active, int32_t* nactive, int* err, uint32_t flags,
+                       hipStream_t s);
+hipError_t launch_combine(const uint16_t* y, const uint16_t* rw, const uint16_t* residual,
+                          uint16_t* out, int T, int K, int H, hipStream_t s);
+hipError_t launch_dequant(const uint8_t* nib, const uint8_t* sc, int rows, int cols, int fmt,
+                          uint16_t* out, hipStream_t s);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,214 @@
+"""Thin ctypes binding of ``libmoe_w4a16.so`` (see ``include/moe_w4a16.h``).
+
+Argument marshalling only: every step of the MoE path runs in the library's
+HIP kernels.  Functions carry the C names; tensors are torch tensors on the
+GPU (any object with ``data_ptr()`` works), ``None`` becomes NULL.  A nonzero
+return code raises :class:`MoeError` with the library's message.  The
+library must have been built (``python -m packed_bit_expert_amd.build``);
+there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_w4a16.so")
+
+ABI_VERSION = 1
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_UNSUPPORTED_SHAPE = -2
+ERR_MISALIGNED = -3
+ERR_WORKSPACE_TOO_SMALL = -4
+ERR_ABI_MISMATCH = -5
+ERR_HIP = -6
+ERR_DEVICE_CHECK = -7
+
+SCALE_E8M0_G32 = 0
+SCALE_E4M3_G16 = 1
+
+FLAG_PRENORM = 1 << 0
+FLAG_FORCE_DECODE = 1 << 1
+FLAG_FORCE_BATCHED = 1 << 2
+FLAG_CHECK_IDS = 1 << 3
+
+EXPORTS = [
+    "moe_w4a16_abi_version", "moe_w4a16_last_error", "moe_w4a16_shape_supported",
+    "moe_w4a16_workspace_bytes", "moe_w4a16_workspace_init", "moe_w4a16_forward",
+    "moe_w4a16_forward_debug", "moe_w4a16_stack_forward", "moe_w4a16_dequant",
+    "moe_w4a16_combine", "moe_w4a16_sort_pairs", "moe_w4a16_device_status",
+    "moe_w4a16_stream_read",
+]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class Cfg(C.Structure):
+    _fields_ = [
+        ("abi_version", C.c_int32), ("num_tokens", C.c_int32), ("hidden", C.c_int32),
+        ("inter", C.c_int32), ("num_experts", C.c_int32), ("top_k", C.c_int32),
+        ("scale_fmt", C.c_int32), ("flags", C.c_uint32), ("tensor_scales", C.c_void_p),
+        ("residual", C.c_void_p), ("prenorm_eps", C.c_float), ("reserved0", C.c_int32),
+        ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t), ("stream", C.c_void_p),
+    ]
+
+
+class Dump(C.Structure):
+    _fields_ = [("u", C.c_void_p), ("g", C.c_void_p), ("v", C.c_void_p), ("h", C.c_void_p),
+                ("y", C.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m packed_bit_expert_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        P, I32, SZ = C.c_void_p, C.c_int32, C.c_size_t
+        sig = {
+            "moe_w4a16_abi_version": (C.c_int, []),
+            "moe_w4a16_last_error": (C.c_char_p, []),
+            "moe_w4a16_shape_supported": (C.c_int, [I32, I32]),
+            "moe_w4a16_workspace_bytes": (SZ, [C.POINTER(Cfg)]),
+            "moe_w4a16_workspace_init": (C.c_int, [P, SZ, P]),
+            "moe_w4a16_forward": (C.c_int, [P, P, P, P, P, P, C.POINTER(Cfg)]),
+            "moe_w4a16_forward_debug": (C.c_int, [P, P, P, P, P, P, C.POINTER(Cfg), C.POINTER(Dump)]),
+            "moe_w4a16_stack_forward": (C.c_int, [I32, P, P, P, P, P, P, P, C.POINTER(Cfg)]),
+            "moe_w4a16_dequant": (C.c_int, [P, P, I32, I32, I32, P, P]),
+            "moe_w4a16_combine": (C.c_int, [P, P, P, P, I32, I32, I32, P]),
+            "moe_w4a16_sort_pairs": (C.c_int, [P, I32, I32, I32, P, P, P, P]),
+            "moe_w4a16_device_status": (C.c_int, [P, C.POINTER(C.c_int32), P]),
+            "moe_w4a16_stream_read": (C.c_int, [P, SZ, P, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        if L.moe_w4a16_abi_version() != ABI_VERSION:
+            raise RuntimeError("libmoe_w4a16.so ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def _p(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise MoeError(rc, lib().moe_w4a16_last_error().decode())
+
+
+def make_cfg(num_tokens, hidden=2048, inter=1536, num_experts=64, top_k=4,
+             scale_fmt=SCALE_E8M0_G32, flags=0, tensor_scales=None, residual=None,
+             prenorm_eps=1e-5, workspace=None, workspace_bytes=None, stream=0) -> Cfg:
+    """Fill a cfg struct; ``stream`` 0 means the default stream, None means
+    torch's current stream."""
+    c = Cfg()
+    c.abi_version = ABI_VERSION
+    c.num_tokens = num_tokens
+    c.hidden, c.inter = hidden, inter
+    c.num_experts, c.top_k = num_experts, top_k
+    c.scale_fmt = scale_fmt
+    c.flags = flags
+    c.tensor_scales = _p(tensor_scales)
+    c.residual = _p(residual)
+    c.prenorm_eps = prenorm_eps
+    c.workspace = _p(workspace)
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    c.workspace_bytes = workspace_bytes
+    c.stream = _stream(stream) if stream != 0 else None
+    return c
+
+
+# -- the C entry points ------------------------------------------------------------------
+
+def moe_w4a16_abi_version() -> int:
+    return lib().moe_w4a16_abi_version()
+
+
+def moe_w4a16_last_error() -> str:
+    return lib().moe_w4a16_last_error().decode()
+
+
+def moe_w4a16_shape_supported(hidden: int, inter: int) -> bool:
+    return bool(lib().moe_w4a16_shape_supported(hidden, inter))
+
+
+def moe_w4a16_workspace_bytes(cfg: Cfg) -> int:
+    return lib().moe_w4a16_workspace_bytes(C.byref(cfg))
+
+
+def moe_w4a16_workspace_init(workspace, nbytes: int, stream=0):
+    _check(lib().moe_w4a16_workspace_init(_p(workspace), nbytes, None if stream == 0 else _stream(stream)))
+
+
+def moe_w4a16_forward(x, expert_ids, route_w, packed_weights, scales, out, cfg: Cfg):
+    _check(lib().moe_w4a16_forward(_p(x), _p(expert_ids), _p(route_w), _p(packed_weights),
+                                   _p(scales), _p(out), C.byref(cfg)))
+
+
+def moe_w4a16_forward_debug(x, expert_ids, route_w, packed_weights, scales, out, cfg: Cfg,
+                            u=None, g=None, v=None, h=None, y=None):
+    d = Dump(_p(u), _p(g), _p(v), _p(h), _p(y))
+    _check(lib().moe_w4a16_forward_debug(_p(x), _p(expert_ids), _p(route_w), _p(packed_weights),
+                                         _p(scales), _p(out), C.byref(cfg), C.byref(d)))
+
+
+def moe_w4a16_stack_forward(num_layers, x, expert_ids, route_w, packed_weights, scales,
+                            tensor_scales, out, cfg: Cfg):
+    _check(lib().moe_w4a16_stack_forward(num_layers, _p(x), _p(expert_ids), _p(route_w),
+                                         _p(packed_weights), _p(scales), _p(tensor_scales),
+                                         _p(out), C.byref(cfg)))
+
+
+def moe_w4a16_dequant(nibbles, scales, rows, cols, scale_fmt, out, stream=0):
+    _check(lib().moe_w4a16_dequant(_p(nibbles), _p(scales), rows, cols, scale_fmt, _p(out),
+                                   None if stream == 0 else _stream(stream)))
+
+
+def moe_w4a16_combine(y, route_w, residual, out, num_tokens, top_k, hidden, stream=0):
+    _check(lib().moe_w4a16_combine(_p(y), _p(route_w), _p(residual), _p(out), num_tokens, top_k,
+                                   hidden, None if stream == 0 else _stream(stream)))
+
+
+def moe_w4a16_sort_pairs(expert_ids, num_tokens, top_k, num_experts, counts, offsets, perm,
+                         stream=0):
+    _check(lib().moe_w4a16_sort_pairs(_p(expert_ids), num_tokens, top_k, num_experts, _p(counts),
+                                      _p(offsets), _p(perm), None if stream == 0 else _stream(stream)))
+
+
+def moe_w4a16_device_status(workspace, stream=0) -> int:
+    code = C.c_int32(0)
+    rc = lib().moe_w4a16_device_status(_p(workspace), C.byref(code),
+                                       None if stream == 0 else _stream(stream))
+    if rc not in (OK, ERR_DEVICE_CHECK):
+        _check(rc)
+    return code.value
+
+
+def moe_w4a16_stream_read(src, nbytes, sink, stream=0):
+    _check(lib().moe_w4a16_stream_read(_p(src), nbytes, _p(sink),
+                                       None if stream == 0 else _stream(stream)))

@@ -1,0 +1,227 @@
+"""GPU: HIP-graph replay with dynamic ids and pointer tables, and the
+38-layer MoE stack at its full size in the configuration the benchmark times.
+
+"LFM2.5-24B-A2B -- Packed MXFP4 Inference": expert selection is recomputed
+on every replay of a captured graph ("GPU routing inside resident-layer
+graphs") and resident experts are read through persistent device pointer
+tables whose entries may change ("Validation": dynamic GPU pointer updates).
+"""
+import numpy as np
+import pytest
+import torch
+
+from packed_bit_expert_amd import moe as M
+from packed_bit_expert_amd import synth as S
+from packed_bit_expert_amd.residency import ResidentExperts
+from tests import gpu_helpers as GH
+
+pytestmark = pytest.mark.gpu
+LFM = S.LFM24B
+
+
+def banner(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+class Bound:
+    """Persistent device buffers of one forward call, for capture."""
+
+    def __init__(self, layer, T, flags=0):
+        sh = LFM
+        self.layer = layer
+        self.x = torch.empty((T, sh.hidden), dtype=torch.bfloat16, device=GH.dev())
+        self.ids = torch.zeros((T, 4), dtype=torch.int32, device=GH.dev())
+        self.rw = torch.empty((T, 4), dtype=torch.bfloat16, device=GH.dev())
+        self.out = torch.empty((T, sh.hidden), dtype=torch.bfloat16, device=GH.dev())
+        self.wtab = layer.wtab.clone()
+        self.stab = layer.stab.clone()
+        self.T, self.flags = T, flags
+
+    def cfg(self, stream):
+        c = M.make_cfg(self.T, flags=self.flags, stream=stream)
+        self.ws = getattr(self, "ws", None)
+        if self.ws is None:
+            self.ws = torch.zeros(M.moe_w4a16_workspace_bytes(c), dtype=torch.uint8, device=GH.dev())
+        c.workspace, c.workspace_bytes = self.ws.data_ptr(), self.ws.numel()
+        return c
+
+    def set(self, x, ids, rw):
+        self.x.copy_(GH.bf16_dev(x))
+        self.ids.copy_(GH.i32_dev(ids))
+        self.rw.copy_(GH.bf16_dev(rw))
+
+    def run(self, stream):
+        M.moe_w4a16_forward(self.x, self.ids, self.rw, self.wtab, self.stab, self.out,
+                            self.cfg(stream))
+
+
+@pytest.fixture(scope="module")
+def layer_mx():
+    banner("upload LFM 2048/1536 E8M0 layer 3")
+    return GH.Layer(LFM, S.FMT_E8M0_G32, 3)
+
+
+@pytest.mark.parametrize("workload", ["c0", "c2"])
+def test_graph_replay_dynamic_ids_and_tables(layer_mx, workload):
+    w = S.WORKLOADS[workload]
+    banner(f"graph replay {workload} T={w.tokens}")
+    B = Bound(layer_mx, w.tokens)
+    s = torch.cuda.Stream()
+    B.set(*S.inputs(w, 3, 0))
+    with torch.cuda.stream(s):
+        B.run(s)  # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        B.run(s)
+    torch.cuda.synchronize()
+    swap = None
+    for step in range(1, 5):
+        x, ids, rw = S.inputs(w, 3, step)
+        if step == 3:  # swap two table entries between replays; the swap stays
+            a, b = int(ids[0, 0]), int((ids[0, 0] + 1) % LFM.experts)
+            for tab in (B.wtab, B.stab):
+                ta, tb = tab[a].clone(), tab[b].clone()
+                tab[a], tab[b] = tb, ta
+            swap = (a, b)
+        B.set(x, ids, rw)
+        g.replay()
+        torch.cuda.synchronize()
+        got = GH.bits_host(B.out)
+        # eager call with the same inputs and tables, into another output
+        e_out = torch.empty_like(B.out)
+        cfg = M.make_cfg(w.tokens)
+        ws = torch.zeros(M.moe_w4a16_workspace_bytes(cfg), dtype=torch.uint8, device=GH.dev())
+        cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), ws.numel()
+        M.moe_w4a16_forward(B.x, B.ids, B.rw, B.wtab, B.stab, e_out, cfg)
+        torch.cuda.synchronize()
+        assert np.array_equal(got, GH.bits_host(e_out)), f"replay {step}"
+        ref_ids = ids
+        if swap is not None:  # the tables route id a to expert b and b to a
+            a, b = swap
+            ref_ids = np.where(ids == a, b, np.where(ids == b, a, ids)).astype(np.int32)
+        GH.compare(got, layer_mx.oracle(x, ref_ids, rw), f"replay{step}")
+
+
+@pytest.fixture(scope="module")
+def stack_store():
+    banner("upload the 38-layer E8M0 stack (12.19 GB)")
+    st = ResidentExperts(LFM, S.FMT_E8M0_G32, LFM.layers).fill_synthetic()
+    yield st
+    del st
+    torch.cuda.empty_cache()
+
+
+def _stack_inputs(w, step, T, L):
+    x = S.activations(w.family, 0, step, T, LFM.hidden)
+    ids, rw = zip(*[S.routing(w, l, step, tokens=T) for l in range(L)])
+    return x, np.stack(ids), np.stack(rw)
+
+
+def _chain_single(store, x, ids, rw, T, eps=GH.EPS):
+    """The stack as L separate single-layer calls (pre-norm + residual)."""
+    h = GH.bf16_dev(x)
+    outs = []
+    for l in range(ids.shape[0]):
+        wt, stb, _ = store.layer_tables(l)
+        out = torch.empty_like(h)
+        cfg = M.make_cfg(T, flags=M.FLAG_PRENORM, residual=h, prenorm_eps=eps)
+        ws = torch.zeros(M.moe_w4a16_workspace_bytes(cfg), dtype=torch.uint8, device=GH.dev())
+        cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), ws.numel()
+        M.moe_w4a16_forward(h, GH.i32_dev(ids[l]), GH.bf16_dev(rw[l]), wt, stb, out, cfg)
+        outs.append(out)
+        h = out
+    torch.cuda.synchronize()
+    return [GH.bits_host(o) for o in outs]
+
+
+def _stack(store, x, ids, rw, T, L):
+    out = torch.empty((T, LFM.hidden), dtype=torch.bfloat16, device=GH.dev())
+    cfg = M.make_cfg(T, prenorm_eps=GH.EPS)
+    ws = torch.zeros(M.moe_w4a16_workspace_bytes(cfg), dtype=torch.uint8, device=GH.dev())
+    cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), ws.numel()
+    M.moe_w4a16_stack_forward(L, GH.bf16_dev(x), GH.i32_dev(ids), GH.bf16_dev(rw), store.wtab,
+                              store.stab, None, out, cfg)
+    torch.cuda.synchronize()
+    return GH.bits_host(out)
+
+
+def _teacher_forced(store, x, ids, rw, layers, what):
+    """Every layer checked on the oracle chain's input: the GPU layer l runs
+    on the oracle's h_l (GPU inputs may come from the oracle; nothing flows
+    the other way) and must match the oracle's h_{l+1}."""
+    h = x
+    worst = 0.0
+    for l in range(layers):
+        lay = GH.Layer(LFM, S.FMT_E8M0_G32, l, store=store, l=l)
+        nxt = lay.oracle(h, ids[l], rw[l], residual=h, prenorm=True)
+        got, st = lay.gpu(h, ids[l], rw[l], residual=h, flags=M.FLAG_PRENORM)
+        s = GH.compare(got, nxt, f"{what} layer{l}")
+        worst = max(worst, s["rel_l2"])
+        h = nxt
+    print(f"[parity] {what}: worst per-layer rel_l2 {worst:.3e}", flush=True)
+    return h
+
+
+def test_c1_stack_full_size(stack_store):
+    """c1 at full size: 38 layers, T=1, one decode step, as the benchmark runs
+    it.  The one-launch stack call equals 38 single-layer calls bit for bit;
+    each layer matches the oracle on the oracle chain's input; the
+    free-running drift of the whole chain is reported."""
+    w = S.WORKLOADS["c1"]
+    L = LFM.layers
+    for step in (0, 1):
+        banner(f"c1 stack step {step}")
+        x, ids, rw = _stack_inputs(w, step, 1, L)
+        got = _stack(stack_store, x, ids, rw, 1, L)
+        chain = _chain_single(stack_store, x, ids, rw, 1)
+        assert np.array_equal(got, chain[-1]), "stack call == 38 single-layer calls"
+        ref = _teacher_forced(stack_store, x, ids, rw, L, f"c1 step{step}")
+        GH.compare(got, ref, "c1 free-running 38-layer drift", check=False)
+
+
+def test_c2_stack_batched(stack_store):
+    """c2 through all 38 layers (T=32, Zipf): the stack call equals the
+    chained single-layer calls; the first 4 layers match the oracle on the
+    oracle chain's input."""
+    w = S.WORKLOADS["c2"]
+    L = LFM.layers
+    banner("c2 stack T=32")
+    x, ids, rw = _stack_inputs(w, 0, 32, L)
+    got = _stack(stack_store, x, ids, rw, 32, L)
+    chain = _chain_single(stack_store, x, ids, rw, 32)
+    assert np.array_equal(got, chain[-1])
+    _teacher_forced(stack_store, x, ids, rw, 4, "c2")
+
+
+def test_stack_graph_replay(stack_store):
+    w = S.WORKLOADS["c1"]
+    L = LFM.layers
+    banner("c1 stack under graph capture, 3 replays")
+    T = 1
+    xd = torch.empty((T, LFM.hidden), dtype=torch.bfloat16, device=GH.dev())
+    idd = torch.zeros((L, T, 4), dtype=torch.int32, device=GH.dev())
+    rwd = torch.empty((L, T, 4), dtype=torch.bfloat16, device=GH.dev())
+    out = torch.empty_like(xd)
+    s = torch.cuda.Stream()
+    cfg = M.make_cfg(T, prenorm_eps=GH.EPS, stream=s)
+    ws = torch.zeros(M.moe_w4a16_workspace_bytes(cfg), dtype=torch.uint8, device=GH.dev())
+    cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), ws.numel()
+
+    def run():
+        M.moe_w4a16_stack_forward(L, xd, idd, rwd, stack_store.wtab, stack_store.stab, None, out, cfg)
+
+    x, ids, rw = _stack_inputs(w, 5, T, L)
+    xd.copy_(GH.bf16_dev(x)); idd.copy_(GH.i32_dev(ids)); rwd.copy_(GH.bf16_dev(rw))
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        run()
+    for step in (6, 7, 8):
+        x, ids, rw = _stack_inputs(w, step, T, L)
+        xd.copy_(GH.bf16_dev(x)); idd.copy_(GH.i32_dev(ids)); rwd.copy_(GH.bf16_dev(rw))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(GH.bits_host(out), _stack(stack_store, x, ids, rw, T, L))
