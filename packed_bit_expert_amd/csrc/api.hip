@@ -41,8 +41,10 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 // Workspace regions (offsets from the base, each 256-byte aligned).
+constexpr int kStackGroup = 64;  // layers whose routing slots are resolved in one pass
+
 struct Layout {
-  size_t meta, perm, hbuf, ybuf, ping, total;
+  size_t meta, perm, hbuf, ybuf, ping, slots, total;
 };
 
 Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
@@ -58,6 +60,8 @@ Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
   off += align256((size_t)(T * K * H) * 2);
   L.ping = off;
   off += align256((size_t)(T * H) * 2);
+  L.slots = off;
+  off += align256((size_t)(T * K) * kStackGroup * sizeof(SlotRef));
   L.total = off;
   return L;
 }
@@ -142,7 +146,7 @@ int check_call(const moe_w4a16_cfg* c, const Call& k) {
   return MOE_OK;
 }
 
-int run_layer(const moe_w4a16_cfg* c, const Call& k) {
+int run_layer(const moe_w4a16_cfg* c, const Call& k, const SlotRef* pre = nullptr) {
   const int T = c->num_tokens;
   if (T == 0) return ok();
   hipStream_t s = (hipStream_t)c->stream;
@@ -162,6 +166,8 @@ int run_layer(const moe_w4a16_cfg* c, const Call& k) {
     a.residual = (const uint16_t*)k.residual;
     a.out = (uint16_t*)k.out;
     a.hbuf = (uint16_t*)(ws + L.hbuf);
+    a.slots = (SlotRef*)(ws + L.slots);
+    a.pre = pre;
     a.du = d ? (uint16_t*)d->u : nullptr;
     a.dg = d ? (uint16_t*)d->g : nullptr;
     a.dv = d ? (uint16_t*)d->v : nullptr;
@@ -281,15 +287,29 @@ int moe_w4a16_stack_forward(int32_t num_layers, const void* x, const int32_t* ex
   if (T == 0) return ok();
   const Layout L = layout(T, lc.hidden, lc.inter, E, K);
   void* ping = (uint8_t*)lc.workspace + L.ping;
+  SlotRef* slots = (SlotRef*)((uint8_t*)lc.workspace + L.slots);
+  int* err = &((Ctrl*)lc.workspace)->err;
+  const bool decode = use_decode(&lc);
   const void* src = x;
   for (int l = 0; l < num_layers; ++l) {
+    const int g = l % kStackGroup;
+    if (decode && g == 0) {
+      // the routing slots of the next (up to) 64 layers, resolved in one pass
+      const int nl = num_layers - l < kStackGroup ? num_layers - l : kStackGroup;
+      hipError_t e = launch_resolve(
+          expert_ids + (size_t)l * T * K, (const uint8_t* const*)(packed_weights + (size_t)l * E),
+          (const uint8_t* const*)(scales + (size_t)l * E),
+          tensor_scales ? tensor_scales + (size_t)l * E * 2 : nullptr, (int)(nl * T * K),
+          (int)(T * K), (int)E, lc.flags, err, slots, (hipStream_t)lc.stream);
+      if (e != hipSuccess) return hip_fail(e, "slot resolve launch");
+    }
     void* dst = ((num_layers - 1 - l) % 2 == 0) ? out : ping;
     lc.residual = src;
     lc.tensor_scales = tensor_scales ? tensor_scales + (size_t)l * E * 2 : nullptr;
     Call kl{src, expert_ids + (size_t)l * T * K, (const uint16_t*)route_w + (size_t)l * T * K,
             packed_weights + (size_t)l * E, scales + (size_t)l * E, lc.tensor_scales, src, dst,
             nullptr};
-    rc = run_layer(&lc, kl);
+    rc = run_layer(&lc, kl, decode ? slots + (size_t)g * T * K : nullptr);
     if (rc) return rc;
     src = dst;
   }

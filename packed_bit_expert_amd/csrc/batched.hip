@@ -108,13 +108,13 @@ __device__ __forceinline__ void load_step(Step& st, const uint8_t* const (&wrow)
                                           const uint8_t* const (&srow)[2], int ks, int g) {
 #pragma unroll
   for (int mt = 0; mt < NMAT; ++mt) {
-    const uint4* src = (const uint4*)(wrow[mt] + ks * (kKS / 2) + 32 * g);
-    st.w[mt][0] = src[0];
-    st.w[mt][1] = src[1];
+    const uint8_t* src = wrow[mt] + ks * (kKS / 2) + 32 * g;
+    st.w[mt][0] = ldg16(src);
+    st.w[mt][1] = ldg16(src + 16);
     if constexpr (FMT == MOE_SCALE_E8M0_G32)
-      st.s[mt] = *(const uint16_t*)(srow[mt] + ks * (kKS / 32) + 2 * g);
+      st.s[mt] = ldg<uint16_t>(srow[mt] + ks * (kKS / 32) + 2 * g);
     else
-      st.s[mt] = *(const uint32_t*)(srow[mt] + ks * (kKS / 16) + 4 * g);
+      st.s[mt] = ldg<uint32_t>(srow[mt] + ks * (kKS / 16) + 4 * g);
   }
 }
 
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(kBT) void k_bat_gemm(BatchedArgs a) {
       if (r < mcnt) {
         const int pair = a.perm[off + mc0 + r];
         const uint16_t* src = MODE == 0 ? a.x + (size_t)(pair / a.K) * Kd : a.hbuf + (size_t)pair * Kd;
-        v = *(const uint4*)(src + 8 * k8);
+        v = ldg16(src + 8 * k8);
       }
       *(uint4*)(xs + r * ldx + 8 * k8) = v;
     }
@@ -238,8 +238,7 @@ __global__ __launch_bounds__(kBT) void k_bat_gemm(BatchedArgs a) {
             const double f = bf2f(row[k]);
             ss += f * f;
           }
-#pragma unroll
-          for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+          ss = seg_finish<32, double>(ss, lane);
           const double den = sqrt(ss / (double)Kd + (double)a.eps);
           for (int k = lane; k < Kd; k += 64) row[k] = f64_to_bf16((double)bf2f(row[k]) / den);
         }

@@ -22,32 +22,41 @@ namespace moe {
 
 namespace {
 
-constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
+// Row mapping shared by both GEMVs.  A row of K = 32*C weights is C 16-byte
+// chunks; LPR lanes share a row, each holding CPL chunks (lane li of the row
+// takes chunks li, li + LPR, ...), so a wave covers RPS = 64 / LPR rows per
+// load set of CPL loads.  Every load instruction still reads contiguous
+// 16*LPR-byte runs of RPS rows.  A lane sums its CPL chunks in registers, so
+// the cross-lane reduction spans only LPR lanes.
+template <int C>
+struct RowMap {
+  static constexpr int LPR = (C % 16 == 0) ? 16 : 8;
+  static_assert(C % LPR == 0, "rows must be a multiple of 8 chunks (256 values)");
+  static constexpr int CPL = C / LPR;
+  static constexpr int RPS = 64 / LPR;
+};
 
-// gate/up: K = H.  One row has C chunks; a wave covers RW rows of gate and of
-// up (8 chunk loads per lane); C divides 64, so a lane always meets the same
-// activation chunk (lane % C) and keeps it in 16 registers.
+// gate/up: K = H; NS load sets per wave (8 loads per lane in total); rows of
+// a set alternate gate n, up n, gate n+1, up n+1, ... so the partner matrix of
+// a row sits LPR lanes away.
 template <int H>
 struct GuShape {
   static constexpr int C = H / 32;
-  static_assert(C >= 8 && C <= 64 && (C & (C - 1)) == 0, "gate/up rows of 8..64 chunks");
-  static constexpr int RW = 256 / C;
-  static constexpr int RWG = 4 * RW;  // rows per 256-thread workgroup
+  using M = RowMap<C>;
+  static constexpr int NS = 8 / M::CPL > 0 ? 8 / M::CPL : 1;
+  static constexpr int RW = NS * M::RPS / 2;  // n rows (of gate and of up) per wave
+  static_assert(NS <= M::LPR && (NS & (NS - 1)) == 0, "load sets per wave");
 };
 
-// down: K = I.  A pattern of L loads per lane covers R whole rows (the chunk a
-// lane meets repeats every L loads); P patterns give ROWS rows per wave.  A
-// workgroup owns ROWS output rows for every slot (one wave per slot), so the
-// combine is finished in the same workgroup.
+// down: K = I; a workgroup owns ROWS = NS * RPS output rows for every slot
+// (one wave per slot), so the combine is finished in the same workgroup.
 template <int I>
 struct DnShape {
   static constexpr int C = I / 32;
-  static constexpr int L = C / gcd_c(C, 64);
-  static constexpr int R = 64 * L / C;
-  static constexpr int P = R >= 8 ? 1 : 8 / R;
-  static constexpr int ROWS = R * P;
-  static constexpr int NL = L * P;
-  static_assert(ROWS <= 64 && (ROWS & (ROWS - 1)) == 0, "rows per wave");
+  using M = RowMap<C>;
+  static constexpr int NS = M::RPS >= 8 ? 1 : 8 / M::RPS;
+  static constexpr int ROWS = NS * M::RPS;
+  static_assert(NS <= M::LPR && (NS & (NS - 1)) == 0, "load sets per wave");
 };
 
 template <int FMT>
@@ -55,15 +64,14 @@ constexpr int group_of() { return FMT == MOE_SCALE_E4M3_G16 ? 16 : 32; }
 
 template <int FMT>
 __device__ __forceinline__ uint32_t load_chunk_scale(const uint8_t* srow, int c) {
-  if constexpr (FMT == MOE_SCALE_E8M0_G32) return srow[c];
-  else return *(const uint16_t*)(srow + 2 * c);
+  if constexpr (FMT == MOE_SCALE_E8M0_G32) return ldg<uint8_t>(srow + c);
+  else return ldg<uint16_t>(srow + 2 * c);
 }
 
 __device__ __forceinline__ void unpack16(const uint16_t* p, bf16x2 (&xp)[16]) {
-  const uint4* v = (const uint4*)p;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint4 w = v[q];
+    const uint4 w = ldg16(p + 8 * q);
     xp[4 * q + 0] = __builtin_bit_cast(bf16x2, w.x);
     xp[4 * q + 1] = __builtin_bit_cast(bf16x2, w.y);
     xp[4 * q + 2] = __builtin_bit_cast(bf16x2, w.z);
@@ -71,205 +79,304 @@ __device__ __forceinline__ void unpack16(const uint16_t* p, bf16x2 (&xp)[16]) {
   }
 }
 
-// Resolves slot (t, j) to its expert's bases; with MOE_FLAG_CHECK_IDS an
-// out-of-range id or a misaligned base marks the slot bad (its h and y are 0).
-__device__ __forceinline__ bool resolve_expert(const DecodeArgs& a, int t, int j, int& e,
-                                               const uint8_t*& wb, const uint8_t*& sb,
-                                               bool report) {
-  e = a.ids[t * a.K + j];
-  wb = nullptr;
-  sb = nullptr;
-  if (a.flags & MOE_FLAG_CHECK_IDS) {
-    if (e < 0 || e >= a.E) {
-      if (report) atomicOr(a.err, kErrBadId);
-      e = 0;
-      return false;
-    }
-    wb = a.wtab[e];
-    sb = a.stab[e];
-    if ((((uintptr_t)wb) | ((uintptr_t)sb)) & 15u) {
-      if (report) atomicOr(a.err, kErrAlign);
-      return false;
-    }
-    return true;
+__device__ __forceinline__ void unpack16_lds(const uint16_t* p, bf16x2 (&xp)[16]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 w = ((const uint4*)p)[q];
+    xp[4 * q + 0] = __builtin_bit_cast(bf16x2, w.x);
+    xp[4 * q + 1] = __builtin_bit_cast(bf16x2, w.y);
+    xp[4 * q + 2] = __builtin_bit_cast(bf16x2, w.z);
+    xp[4 * q + 3] = __builtin_bit_cast(bf16x2, w.w);
   }
-  wb = a.wtab[e];
-  sb = a.stab[e];
-  return true;
 }
 
-// Grouped gate/up GEMV + silu(g) * u for one (token, slot, row block).
-template <int H, int FMT>
+// Resolves slot i of ids/wtab/stab to its expert.  With MOE_FLAG_CHECK_IDS an
+// out-of-range id or a misaligned base marks the slot bad (ok = 0) and, when
+// err is not null, sets the matching device error bit.
+__device__ __forceinline__ SlotRef resolve_slot(const int32_t* ids, const uint8_t* const* wtab,
+                                                const uint8_t* const* stab, const float* tsc,
+                                                int i, int E, uint32_t flags, int* err) {
+  SlotRef r;
+  r.pad = 0;
+  r.tg = r.td = 1.f;
+  const int e = ids[i];
+  if ((flags & MOE_FLAG_CHECK_IDS) && (e < 0 || e >= E)) {
+    if (err) atomicOr(err, kErrBadId);
+    r.w = r.s = nullptr;
+    r.ok = 0;
+    return r;
+  }
+  r.w = wtab[e];
+  r.s = stab[e];
+  r.ok = 1;
+  if ((flags & MOE_FLAG_CHECK_IDS) && ((((uintptr_t)r.w) | ((uintptr_t)r.s)) & 15u)) {
+    if (err) atomicOr(err, kErrAlign);
+    r.ok = 0;
+  }
+  if (tsc && r.ok) {
+    r.tg = tsc[2 * e];
+    r.td = tsc[2 * e + 1];
+  }
+  return r;
+}
+
+// Slots of consecutive layers resolved in one pass (the layer-stack path):
+// the per-layer kernels then need one dependent load before streaming.
+__global__ __launch_bounds__(256) void k_resolve(const int32_t* ids, const uint8_t* const* wtab,
+                                                 const uint8_t* const* stab, const float* tsc,
+                                                 int n, int per_layer, int E, uint32_t flags,
+                                                 int* err, SlotRef* out) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int l = i / per_layer;
+  out[i] = resolve_slot(ids + (size_t)l * per_layer, wtab + (size_t)l * E, stab + (size_t)l * E,
+                        tsc ? tsc + (size_t)l * E * 2 : nullptr, i - l * per_layer, E, flags, err);
+}
+
+__device__ __forceinline__ SlotRef load_slot(const SlotRef* p) {
+  // one 32-byte vector load
+  SlotRef r;
+  const uint4* q = (const uint4*)p;
+  const uint4 a = q[0], b = q[1];
+  r.w = (const uint8_t*)(((uint64_t)a.y << 32) | a.x);
+  r.s = (const uint8_t*)(((uint64_t)a.w << 32) | a.z);
+  r.tg = __uint_as_float(b.x);
+  r.td = __uint_as_float(b.y);
+  r.ok = (int32_t)b.z;
+  r.pad = 0;
+  return r;
+}
+
+// Grouped gate/up GEMV + silu(g) * v.  A 256-thread workgroup is four
+// independent waves, each owning RW rows of gate and of up of one (token,
+// slot).  All loads of a wave are issued before any arithmetic; the
+// activation slices come first because vmcnt retires loads in issue order.
+// With PRENORM the workgroup stages x in LDS and computes the weightless RMS
+// pre-norm once (FP64) for its four waves.  A rejected slot reads a harmless
+// valid address and writes zeros, so the code after the loads is
+// straight-line and each chunk waits only for its own load.
+template <int H, int FMT, bool PRENORM, bool DUMP>
 __global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
   using S = GuShape<H>;
-  constexpr int C = S::C, RW = S::RW, RWG = S::RWG, G = group_of<FMT>();
-  __shared__ __attribute__((aligned(16))) uint16_t xs[H];
+  using M = typename S::M;
+  constexpr int LPR = M::LPR, CPL = M::CPL, RPS = M::RPS, NS = S::NS, RW = S::RW;
+  constexpr int G = group_of<FMT>();
+  __shared__ __attribute__((aligned(16))) uint16_t xs[PRENORM ? H : 8];
   __shared__ double red[4];
-
   const int I = a.I;
-  const int nblk = (I + RWG - 1) / RWG;
-  int b = blockIdx.x;
-  const int nb = b % nblk;
-  b /= nblk;
-  const int j = b % a.K, t = b / a.K;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int per_slot = (I + RW - 1) / RW;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * 4 + wave;
+  // all waves of a workgroup belong to one token (per_slot * K is a multiple of 4)
+  const int nb = gw % per_slot, sj = gw / per_slot;
+  const bool live = sj < a.T * a.K;
+  const int sjc = live ? sj : a.T * a.K - 1;
+  const int t = sjc / a.K, j = sjc - t * a.K;
 
-  int e;
-  const uint8_t *wb, *sb;
-  const bool ok = resolve_expert(a, t, j, e, wb, sb, tid == 0 && nb == 0);
+  const SlotRef sr = a.pre ? load_slot(a.pre + sjc)
+                           : resolve_slot(a.ids, a.wtab, a.stab, a.tsc, sjc, a.E, a.flags,
+                                          (nb == 0 && lane == 0 && live) ? a.err : nullptr);
+  if (!a.pre && nb == 0 && lane == 0 && live) a.slots[sj] = sr;
+  const bool ok = __builtin_amdgcn_readfirstlane(sr.ok) != 0;
+  const uint8_t* wbase = ok ? sr.w : (const uint8_t*)a.slots;
+  const uint8_t* sbase = ok ? sr.s : (const uint8_t*)a.slots;
+  const size_t mat_nib = ok ? (size_t)I * (H / 2) : 0, mat_sc = ok ? (size_t)I * (H / G) : 0;
+  const size_t row_nib = ok ? H / 2 : 0, row_sc = ok ? H / G : 0;
+  const int li = lane % LPR, q = lane / LPR;
+  const int n0 = nb * RW;
 
-  // 1. issue every weight load of this wave
-  const int n0 = nb * RWG + wave * RW;
-  const size_t mat_nib = (size_t)I * (H / 2), mat_sc = (size_t)I * (H / G);
-  uint4 wv[8];
-  uint32_t sv[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int f = 64 * i + lane;
-    const int r = f / (2 * C), mat = (f / C) & 1, c = f % C;
-    const int n = n0 + r;
-    wv[i] = make_uint4(0u, 0u, 0u, 0u);
-    sv[i] = 0u;
-    if (ok && n < I) {
-      wv[i] = *(const uint4*)(wb + mat * mat_nib + (size_t)n * (H / 2) + 16 * c);
-      sv[i] = load_chunk_scale<FMT>(sb + mat * mat_sc + (size_t)n * (H / G), c);
-    }
-  }
-
-  // 2. stage x (or its weightless RMS pre-norm, in FP64) in LDS
+  // 1. loads: activations first (vmcnt retires loads in issue order, so the
+  // pre-norm or the first chunk can start while the weights stream), then
+  // scale bytes, then weights
   const uint16_t* xt = a.x + (size_t)t * H;
-  const bool prenorm = (a.flags & MOE_FLAG_PRENORM) != 0;
-  double ss = 0.0;
-  for (int k8 = tid; k8 < H / 8; k8 += 256) {
-    const uint4 v = *(const uint4*)(xt + 8 * k8);
-    *(uint4*)(xs + 8 * k8) = v;
-    if (prenorm) {
+  bf16x2 xp[CPL][16];
+  constexpr int XPT = PRENORM ? (H / 8 + 255) / 256 : 1;  // 16-byte pieces of x per thread
+  uint4 xraw[XPT];
+  if constexpr (PRENORM) {
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const int k8 = threadIdx.x + 256 * u;
+      xraw[u] = k8 < H / 8 ? ldg16(xt + 8 * k8) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) unpack16(xt + 32 * (li + LPR * i), xp[i]);
+  }
+  uint4 wv[NS][CPL];
+  uint32_t sv[NS][CPL];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    const int n = min(n0 + st * (RPS / 2) + (q >> 1), I - 1);  // a ragged last wave re-reads row I-1
+    const uint8_t* srow = sbase + (q & 1) * mat_sc + (size_t)n * row_sc;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) sv[st][i] = load_chunk_scale<FMT>(srow, ok ? li + LPR * i : 0);
+  }
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    const int n = min(n0 + st * (RPS / 2) + (q >> 1), I - 1);
+    const uint8_t* wrow = wbase + (q & 1) * mat_nib + (size_t)n * row_nib;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) wv[st][i] = ldg16(wrow + (ok ? 16 * (li + LPR * i) : 0));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. pre-norm once per workgroup (FP64), then the slices from LDS
+  if constexpr (PRENORM) {
+    double ss = 0.0;
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const int k8 = threadIdx.x + 256 * u;
+      if (k8 >= H / 8) break;
+      const uint4 v = xraw[u];
+      *(uint4*)(xs + 8 * k8) = v;
       const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const double lo = __uint_as_float(w4[q] << 16), hi = __uint_as_float(w4[q] & 0xFFFF0000u);
+      for (int k = 0; k < 4; ++k) {
+        const double lo = __uint_as_float(w4[k] << 16), hi = __uint_as_float(w4[k] & 0xFFFF0000u);
         ss += lo * lo + hi * hi;
       }
     }
-  }
-  if (prenorm) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+    ss = seg_finish<32, double>(ss, lane);
     if (lane == 0) red[wave] = ss;
     __syncthreads();
-    const double den = sqrt((red[0] + red[1] + red[2] + red[3]) / (double)H + (double)a.eps);
-    for (int k = tid; k < H; k += 256) xs[k] = f64_to_bf16((double)bf2f(xs[k]) / den);
-  }
-  __syncthreads();
-  if (a.du && nb == 0 && j == 0)
-    for (int k = tid; k < H; k += 256) a.du[(size_t)t * H + k] = xs[k];
-
-  bf16x2 xp[16];
-  unpack16(xs + 32 * (lane % C), xp);
-
-  // 3. dot products, then one butterfly for all 8 chunk sums
-  double p[8];
+    const double rs = 1.0 / sqrt((red[0] + red[1] + red[2] + red[3]) / (double)H + (double)a.eps);
+    for (int k = threadIdx.x; k < H; k += 256) xs[k] = f64_to_bf16((double)bf2f(xs[k]) * rs);
+    __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 8; ++i) p[i] = chunk_dot<FMT>(wv[i], sv[i], xp);
-  const double tot = seg_reduce<8, C>(p, lane);
-  const double oth = __shfl_xor(tot, C == 64 ? 8 : C);  // the same row of the other matrix
+    for (int i = 0; i < CPL; ++i) unpack16_lds(xs + 32 * (li + LPR * i), xp[i]);
+    if constexpr (DUMP) {
+      if (a.du && nb < 4 && j == 0 && live)
+        for (int k = threadIdx.x; k < H; k += 256) a.du[(size_t)t * H + k] = xs[k];
+    }
+  } else if constexpr (DUMP) {
+    if (a.du && nb == 0 && j == 0 && live)
+      for (int k = lane; k < H; k += 64) a.du[(size_t)t * H + k] = xt[k];
+  }
+  if (!live) return;
 
-  const int s = lane / C;
-  const int v = (lane % C) / (C / 8);
-  const int mat = (C == 64) ? (v & 1) : (s & 1);
-  const int r = (C == 64) ? (v >> 1) : (32 / C) * v + (s >> 1);
-  const int n = n0 + r;
-  if ((lane % (C / 8)) == 0 && mat == 0 && n < I) {
-    double tg = 1.0;
-    if constexpr (FMT == MOE_SCALE_E4M3_G16) tg = ok ? (double)a.tsc[2 * e] : 0.0;
+  // 3. dot products (a lane sums its CPL chunks), one butterfly over LPR lanes
+  double p[NS];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    p[st] = 0.0;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) p[st] += chunk_dot<FMT>(wv[st][i], sv[st][i], xp[i]);
+  }
+  const double tot = seg_reduce<NS, LPR>(p, lane);
+  const double oth = xor_lane<LPR>(tot, lane);  // the same n of the other matrix
+  const int v = li / (LPR / NS);             // load set whose sum this lane holds
+  const int n = n0 + v * (RPS / 2) + (q >> 1);
+  if ((li % (LPR / NS)) == 0 && (q & 1) == 0 && n < I) {
+    const double tg = (double)sr.tg;
     uint16_t gb = f64_to_bf16(tot * tg), ub = f64_to_bf16(oth * tg);
     uint16_t h = silu_mul_bf16(gb, ub);
     if (!ok) gb = ub = h = 0;
-    const size_t o = ((size_t)t * a.K + j) * I + n;
+    const size_t o = (size_t)sj * I + n;
     a.hbuf[o] = h;
-    if (a.dg) a.dg[o] = gb;
-    if (a.dv) a.dv[o] = ub;
-    if (a.dh) a.dh[o] = h;
+    if constexpr (DUMP) {
+      if (a.dg) a.dg[o] = gb;
+      if (a.dv) a.dv[o] = ub;
+      if (a.dh) a.dh[o] = h;
+    }
   }
 }
 
-// Grouped down GEMV for ROWS output rows of every slot, then the slot-order
-// BF16 combine (+ residual) of those rows.
-template <int H, int I, int FMT>
+// Grouped down GEMV for ROWS output rows of every slot (one wave per slot),
+// then the slot-order BF16 combine (+ residual) of those rows.
+template <int H, int I, int FMT, bool DUMP>
 __global__ __launch_bounds__(256) void k_dec_down(DecodeArgs a) {
   using D = DnShape<I>;
-  constexpr int C = D::C, L = D::L, R = D::R, ROWS = D::ROWS, NL = D::NL, G = group_of<FMT>();
+  using M = typename D::M;
+  constexpr int LPR = M::LPR, CPL = M::CPL, RPS = M::RPS, NS = D::NS, ROWS = D::ROWS;
+  constexpr int G = group_of<FMT>();
   __shared__ uint16_t ys[8][ROWS];
 
   const int nblk = H / ROWS;
   const int mb = blockIdx.x % nblk, t = blockIdx.x / nblk;
   const int m0 = mb * ROWS;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int li = lane % LPR, q = lane / LPR;
+  const SlotRef* slots = a.pre ? a.pre : a.slots;
+  // the combine's operands are fetched now, not after the reduction
+  uint16_t rwv[8], resv = 0;
+  if (tid < ROWS) {
+    for (int j = 0; j < a.K; ++j) rwv[j] = a.rw[t * a.K + j];
+    if (a.residual) resv = a.residual[(size_t)t * H + m0 + tid];
+  }
 
   for (int j = wave; j < a.K; j += 4) {
-    int e;
-    const uint8_t *wb, *sb;
-    const bool ok = resolve_expert(a, t, j, e, wb, sb, false);
-    const uint8_t* wd = ok ? wb + (size_t)I * H : nullptr;              // after gate and up
-    const uint8_t* sd = ok ? sb + 2 * (size_t)I * (H / G) : nullptr;
-    uint4 wv[NL];
-    uint32_t sv[NL];
-#pragma unroll
-    for (int q = 0; q < NL; ++q) {
-      const int pl = q / L, ql = q % L;
-      const int f = 64 * ql + lane;
-      const int m = m0 + pl * R + f / C, c = f % C;
-      wv[q] = make_uint4(0u, 0u, 0u, 0u);
-      sv[q] = 0u;
-      if (ok) {
-        wv[q] = *(const uint4*)(wd + (size_t)m * (I / 2) + 16 * c);
-        sv[q] = load_chunk_scale<FMT>(sd + (size_t)m * (I / G), c);
-      }
-    }
+    const SlotRef sr = load_slot(slots + t * a.K + j);
+    const bool ok = __builtin_amdgcn_readfirstlane(sr.ok) != 0;
+    // a rejected slot reads a harmless valid address (the slot table)
+    const uint8_t* wd = ok ? sr.w + (size_t)I * H : (const uint8_t*)slots;   // after gate and up
+    const uint8_t* sd = ok ? sr.s + 2 * (size_t)I * (H / G) : (const uint8_t*)slots;
+    const size_t row_nib = ok ? I / 2 : 0, row_sc = ok ? I / G : 0;
+    // h slices first (vmcnt retires loads in issue order), then scales, weights
     const uint16_t* hj = a.hbuf + ((size_t)t * a.K + j) * I;
-    bf16x2 hp[L][16];
+    bf16x2 hp[CPL][16];
 #pragma unroll
-    for (int ql = 0; ql < L; ++ql) unpack16(hj + 32 * ((64 * ql + lane) % C), hp[ql]);
+    for (int i = 0; i < CPL; ++i) unpack16(hj + 32 * (li + LPR * i), hp[i]);
+    uint4 wv[NS][CPL];
+    uint32_t sv[NS][CPL];
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+#pragma unroll
+      for (int i = 0; i < CPL; ++i)
+        sv[st][i] = load_chunk_scale<FMT>(sd + (size_t)(m0 + st * RPS + q) * row_sc,
+                                          ok ? li + LPR * i : 0);
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+#pragma unroll
+      for (int i = 0; i < CPL; ++i)
+        wv[st][i] = ldg16(wd + (size_t)(m0 + st * RPS + q) * row_nib + (ok ? 16 * (li + LPR * i) : 0));
+    __builtin_amdgcn_sched_barrier(0);
 
-    double acc[ROWS];
+    double p[NS];
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) acc[r] = 0.0;
+    for (int st = 0; st < NS; ++st) {
+      p[st] = 0.0;
 #pragma unroll
-    for (int q = 0; q < NL; ++q) {
-      const int pl = q / L, ql = q % L;
-      const double part = chunk_dot<FMT>(wv[q], sv[q], hp[ql]);
-      const int rr = (64 * ql + lane) / C;
-      const int lo = (64 * ql) / C, hi = (64 * ql + 63) / C;  // rows this load can touch
-#pragma unroll
-      for (int r = lo; r <= hi; ++r) acc[pl * R + r] += (rr == r) ? part : 0.0;
+      for (int i = 0; i < CPL; ++i) p[st] += chunk_dot<FMT>(wv[st][i], sv[st][i], hp[i]);
     }
-    const double tot = seg_reduce<ROWS, 64>(acc, lane);
-    if ((lane % (64 / ROWS)) == 0) {
-      const int v = lane / (64 / ROWS);
-      double td = 1.0;
-      if constexpr (FMT == MOE_SCALE_E4M3_G16) td = ok ? (double)a.tsc[2 * e + 1] : 0.0;
-      const uint16_t y = ok ? f64_to_bf16(tot * td) : (uint16_t)0;
-      ys[j][v] = y;
-      if (a.dy) a.dy[((size_t)t * a.K + j) * H + m0 + v] = y;
+    const double tot = seg_reduce<NS, LPR>(p, lane);
+    if ((li % (LPR / NS)) == 0) {
+      const int r = (li / (LPR / NS)) * RPS + q;
+      const uint16_t y = ok ? f64_to_bf16(tot * (double)sr.td) : (uint16_t)0;
+      ys[j][r] = y;
+      if constexpr (DUMP) {
+        if (a.dy) a.dy[((size_t)t * a.K + j) * H + m0 + r] = y;
+      }
     }
   }
   __syncthreads();
   if (tid < ROWS) {
     const int m = m0 + tid;
     uint16_t acc = 0;  // +0
-    for (int j = 0; j < a.K; ++j) acc = combine_step(acc, a.rw[t * a.K + j], ys[j][tid]);
-    if (a.residual) acc = residual_add(a.residual[(size_t)t * H + m], acc);
+    for (int j = 0; j < a.K; ++j) acc = combine_step(acc, rwv[j], ys[j][tid]);
+    if (a.residual) acc = residual_add(resv, acc);
     a.out[(size_t)t * H + m] = acc;
   }
 }
 
+template <int H, int I, int FMT, bool PRENORM, bool DUMP>
+hipError_t launch_variant(const DecodeArgs& a, hipStream_t s) {
+  // the pre-norm is shared by the four waves of a workgroup: they must belong
+  // to one token
+  if (PRENORM && ((I / GuShape<H>::RW) * a.K) % 4 != 0) return hipErrorInvalidValue;
+  const int waves = a.T * a.K * ((I + GuShape<H>::RW - 1) / GuShape<H>::RW);
+  k_dec_gateup<H, FMT, PRENORM, DUMP><<<(waves + 3) / 4, 256, 0, s>>>(a);
+  k_dec_down<H, I, FMT, DUMP><<<a.T * (H / DnShape<I>::ROWS), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 template <int H, int I, int FMT>
 hipError_t launch_shape(const DecodeArgs& a, hipStream_t s) {
-  const int g1 = a.T * a.K * ((I + GuShape<H>::RWG - 1) / GuShape<H>::RWG);
-  k_dec_gateup<H, FMT><<<g1, 256, 0, s>>>(a);
-  const int g2 = a.T * (H / DnShape<I>::ROWS);
-  k_dec_down<H, I, FMT><<<g2, 256, 0, s>>>(a);
-  return hipGetLastError();
+  const bool pre = (a.flags & MOE_FLAG_PRENORM) != 0;
+  const bool dump = a.du || a.dg || a.dv || a.dh || a.dy;
+  if (pre) return dump ? launch_variant<H, I, FMT, true, true>(a, s)
+                       : launch_variant<H, I, FMT, true, false>(a, s);
+  return dump ? launch_variant<H, I, FMT, false, true>(a, s)
+              : launch_variant<H, I, FMT, false, false>(a, s);
 }
 
 template <int FMT>
@@ -284,6 +391,14 @@ hipError_t launch_fmt(const DecodeArgs& a, hipStream_t s) {
 
 bool decode_supported(int H, int I) {
   return (H == 2048 && I == 1536) || (H == 1024 && I == 768) || (H == 512 && I == 256);
+}
+
+hipError_t launch_resolve(const int32_t* ids, const uint8_t* const* wtab,
+                          const uint8_t* const* stab, const float* tsc, int n, int per_layer,
+                          int E, uint32_t flags, int* err, SlotRef* out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  k_resolve<<<(n + 255) / 256, 256, 0, s>>>(ids, wtab, stab, tsc, n, per_layer, E, flags, err, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int fmt, hipStream_t s) {

@@ -7,6 +7,16 @@
 
 namespace moe {
 
+// One routing slot (token t, slot j) resolved to its expert: weight and scale
+// bases and the two tensor scales (1 for E8M0).  ok = 0 marks a slot a device
+// check rejected (its h and y are 0).
+struct SlotRef {
+  const uint8_t* w;
+  const uint8_t* s;
+  float tg, td;
+  int32_t ok, pad;
+};
+
 // Arguments of the per-token GEMV path (decode).  All pointers are device
 // pointers; the dump pointers may be null.
 struct DecodeArgs {
@@ -19,6 +29,8 @@ struct DecodeArgs {
   const uint16_t* residual;   // [T][H] or null
   uint16_t* out;              // [T][H]
   uint16_t* hbuf;             // [T][K][I] workspace
+  SlotRef* slots;             // [T][K] workspace: written by gate/up, read by down
+  const SlotRef* pre;         // [T][K] already resolved slots, or null
   uint16_t *du, *dg, *dv, *dh, *dy;
   int* err;                   // device error word
   int T, H, I, K, E;
@@ -56,6 +68,11 @@ bool batched_supported(int H, int I);
 int batched_chunk_tokens(int H, int I);
 
 hipError_t launch_decode(const DecodeArgs& a, int fmt, hipStream_t s);
+// Resolve n = L*T*K slots of consecutive layers: out[i] for ids[i] of layer
+// i / (T*K), tables wtab/stab [L][E], tensor scales [L][E][2] or null.
+hipError_t launch_resolve(const int32_t* ids, const uint8_t* const* wtab,
+                          const uint8_t* const* stab, const float* tsc, int n, int per_layer,
+                          int E, uint32_t flags, int* err, SlotRef* out, hipStream_t s);
 hipError_t launch_batched(const BatchedArgs& a, int fmt, hipStream_t s);
 hipError_t launch_sort(const int32_t* ids, int npairs, int E, int32_t* counts, int32_t* offsets,
                        int32_t* perm, int32_t* active, int32_t* nactive, int* err, uint32_t flags,
