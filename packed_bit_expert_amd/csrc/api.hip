@@ -44,16 +44,12 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 constexpr int kStackGroup = 64;  // layers whose routing slots are resolved in one pass
 
 struct Layout {
-  size_t meta, perm, hbuf, ybuf, ping, slots, total;
+  size_t hbuf, ybuf, ping, slots, total;
 };
 
 Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
   Layout L;
   size_t off = kCtrlBytes;
-  L.meta = off;  // counts[E], offsets[E+1], active[E], nactive
-  off += align256((size_t)(3 * E + 2) * 4);
-  L.perm = off;
-  off += align256((size_t)(T * K) * 4);
   L.hbuf = off;
   off += align256((size_t)(T * K * I) * 2);
   L.ybuf = off;
@@ -194,12 +190,6 @@ int run_layer(const moe_w4a16_cfg* c, const Call& k, const SlotRef* pre = nullpt
   a.tsc = k.tsc;
   a.residual = (const uint16_t*)k.residual;
   a.out = (uint16_t*)k.out;
-  int32_t* meta = (int32_t*)(ws + L.meta);
-  a.counts = meta;
-  a.offsets = meta + c->num_experts;
-  a.active = meta + 2 * c->num_experts + 1;
-  a.nactive = meta + 3 * c->num_experts + 1;
-  a.perm = (int32_t*)(ws + L.perm);
   a.hbuf = (uint16_t*)(ws + L.hbuf);
   a.ybuf = (uint16_t*)(ws + L.ybuf);
   a.du = d ? (uint16_t*)d->u : nullptr;
@@ -213,7 +203,6 @@ int run_layer(const moe_w4a16_cfg* c, const Call& k, const SlotRef* pre = nullpt
   a.I = c->inter;
   a.K = c->top_k;
   a.E = c->num_experts;
-  a.mc = batched_chunk_tokens(c->hidden, c->inter);
   a.flags = c->flags;
   a.eps = c->prenorm_eps;
   if (c->flags & MOE_FLAG_CHECK_IDS) {

@@ -3,10 +3,11 @@
 // "visible-cx/LFM2.5-8B-A1B-CoreAI", "Provenance": the batched switch-GLU
 // serves S=64 by sorting (token, expert) pairs, so each selected expert's
 // packed weights are read once per call for all of its tokens.  Here:
-//   1. k_sort: stable counting sort of the T*k pairs by expert, on device
-//      (no id or count ever reaches the host: "GPU routing inside
-//      resident-layer graphs" of the MXFP4 card);
-//   2. k_bat_gemm<MODE 0>: per (expert, 128-row tile) workgroup, the expert's
+//   1. grouping: each GEMM workgroup collects its expert's (token, slot)
+//      pairs with a stable on-device scan of the ids (no id or count ever
+//      reaches the host: "GPU routing inside resident-layer graphs" of the
+//      MXFP4 card); k_sort is the same grouping as a stand-alone hook;
+//   2. k_bat_gemm<MODE 0>: per (expert, 64-row tile) workgroup, the expert's
 //      token rows are staged in LDS, packed gate and up rows are dequantised
 //      to BF16 MFMA operands in registers (exact, no BF16 copy in memory),
 //      v_mfma_f32_16x16x32_bf16 accumulates in FP32, and the epilogue writes
@@ -23,9 +24,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kBT = 512;  // threads per GEMM workgroup (8 waves)
-constexpr int kBN = 128;  // output rows per GEMM workgroup (16 per wave)
-constexpr int kKS = 256;  // contraction elements per step (64 per lane group)
+constexpr int kKS = 256;  // contraction elements per GEMM K step (64 per lane group)
 
 // ---------------------------------------------------------------------------
 // 1. stable counting sort of (token, slot) pairs by expert
@@ -92,34 +91,49 @@ __global__ __launch_bounds__(256) void k_sort(const int32_t* __restrict__ ids, i
 // ---------------------------------------------------------------------------
 // 2./3. grouped GEMM on bf16 MFMA
 // ---------------------------------------------------------------------------
-// Lane (n = lane % 16, g = lane / 16) of a wave loads 32 contiguous bytes (64
-// codes) of its weight row per K step: K indices [ks*256 + 64g, +64).  Dword d
-// of that holds K = ks*256 + 64g + 8d + [0, 8), which is the lane's 8-element
-// B operand of MFMA number d; the A operand (token rows in LDS) is read at the
-// same K indices, so every MFMA pairs A and B on identical K (the order of
-// the K terms inside the FP32 sum is the only freedom used).
-struct Step {
-  uint4 w[2][2];  // [matrix][half]
-  uint32_t s[2];  // scale bytes of the 64 codes
+// A workgroup owns (expert e, 64 output rows): four waves of 16 rows.  It
+// first finds e's (token, slot) pairs itself -- a stable ballot scan of the
+// routing ids, so no sort kernel and no host read -- and exits if there are
+// none.  Lane (n = lane % 16, g = lane / 16) loads 32 contiguous bytes (64
+// codes) of its weight row per K step of 256: K indices [ks*256 + 64g, +64).
+// Dword d of that holds K = ks*256 + 64g + 8d + [0, 8), which is the lane's
+// 8-element B operand of MFMA number d; the A operand (token rows in LDS) is
+// read at the same K indices, so every MFMA pairs A and B on identical K (the
+// order of the K terms inside the FP32 sum is the only freedom used).  All
+// KB steps of weights are issued into registers at once, so they are read
+// from HBM once per call however many tokens the expert has; tokens are
+// staged 16 at a time (one MFMA M tile) in LDS.
+constexpr int kBW = 4;        // waves per workgroup
+constexpr int kBN = 16 * kBW; // output rows per workgroup
+constexpr int kMC = 16;       // tokens per LDS pass
+constexpr int kListCap = 2048;  // pair indices collected per scan pass
+
+template <int FMT, int NMAT>
+struct WStep {
+  uint4 w[NMAT][2];
+  uint32_t s[NMAT];
 };
 
 template <int FMT, int NMAT>
-__device__ __forceinline__ void load_step(Step& st, const uint8_t* const (&wrow)[2],
-                                          const uint8_t* const (&srow)[2], int ks, int g) {
+__device__ __forceinline__ void load_wstep(WStep<FMT, NMAT>& st, const uint8_t* const (&wrow)[2],
+                                           const uint8_t* const (&srow)[2], int ks, int g) {
 #pragma unroll
   for (int mt = 0; mt < NMAT; ++mt) {
-    const uint8_t* src = wrow[mt] + ks * (kKS / 2) + 32 * g;
-    st.w[mt][0] = ldg16(src);
-    st.w[mt][1] = ldg16(src + 16);
     if constexpr (FMT == MOE_SCALE_E8M0_G32)
       st.s[mt] = ldg<uint16_t>(srow[mt] + ks * (kKS / 32) + 2 * g);
     else
       st.s[mt] = ldg<uint32_t>(srow[mt] + ks * (kKS / 16) + 4 * g);
   }
+#pragma unroll
+  for (int mt = 0; mt < NMAT; ++mt) {
+    const uint8_t* src = wrow[mt] + ks * (kKS / 2) + 32 * g;
+    st.w[mt][0] = ldg16(src);
+    st.w[mt][1] = ldg16(src + 16);
+  }
 }
 
-template <int FMT>
-__device__ __forceinline__ bf16x8 step_operand(const Step& st, int mt, int d) {
+template <int FMT, int NMAT>
+__device__ __forceinline__ bf16x8 wstep_operand(const WStep<FMT, NMAT>& st, int mt, int d) {
   const uint4& h = st.w[mt][d >> 2];
   const uint32_t w = (d & 3) == 0 ? h.x : (d & 3) == 1 ? h.y : (d & 3) == 2 ? h.z : h.w;
   if constexpr (FMT == MOE_SCALE_E8M0_G32)
@@ -128,73 +142,218 @@ __device__ __forceinline__ bf16x8 step_operand(const Step& st, int mt, int d) {
     return fp4x8_scaled_to_bf16x8(w, e4m3_f32((st.s[mt] >> (8 * (d >> 1))) & 255u));
 }
 
-// MFMAs chained in FP32 before their sum is added to the FP64 accumulators.
-// A short chain of exact BF16 products is exact in FP32 unless it spans more
-// than 24 bits, so the FP64 accumulation keeps the outputs correctly rounded
-// to BF16 almost always (the same scheme as the decode path's runs of 8).
-constexpr int kChain = 1;
-
+// One K step: 8 MFMAs per matrix on one 16-token tile.  Each MFMA's FP32
+// result (32 exact BF16 products) is added to FP64 accumulators, which keeps
+// the BF16 outputs correctly rounded almost always (as in the decode path).
+// Chaining MFMAs in FP32 instead is cheaper but flips output roundings often
+// enough that the slot-order BF16 combine, where slots cancel, turns a flip
+// into an error above the 1% parity bound.
 template <int FMT, int NMAT>
-__device__ __forceinline__ void step_mfma(const Step& st, const uint16_t* xs, int ldx, int ks,
-                                          int ln, int g, bool two, double (&acc)[2][2][4]) {
-  const uint16_t* arow0 = xs + ln * ldx + ks * kKS + 64 * g;
-  const uint16_t* arow1 = arow0 + 16 * ldx;
+__device__ __forceinline__ void wstep_mfma(const WStep<FMT, NMAT>& st, const uint16_t* arow,
+                                           double (&acc)[2][4]) {
 #pragma unroll
-  for (int d0 = 0; d0 < 8; d0 += kChain) {
-    f32x4 part[NMAT][2];
+  for (int d = 0; d < 8; ++d) {
+    const bf16x8 A = *(const bf16x8*)(arow + 8 * d);
 #pragma unroll
-    for (int mt = 0; mt < NMAT; ++mt) part[mt][0] = part[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < NMAT; ++mt) {
+      const f32x4 part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          A, wstep_operand<FMT, NMAT>(st, mt, d), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-    for (int d = d0; d < d0 + kChain; ++d) {
-      bf16x8 B[NMAT];
-#pragma unroll
-      for (int mt = 0; mt < NMAT; ++mt) B[mt] = step_operand<FMT>(st, mt, d);
-      const bf16x8 A0 = *(const bf16x8*)(arow0 + 8 * d);
-#pragma unroll
-      for (int mt = 0; mt < NMAT; ++mt)
-        part[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B[mt], part[mt][0], 0, 0, 0);
-      if (two) {
-        const bf16x8 A1 = *(const bf16x8*)(arow1 + 8 * d);
-#pragma unroll
-        for (int mt = 0; mt < NMAT; ++mt)
-          part[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B[mt], part[mt][1], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) acc[mt][i] += (double)part[i];
+    }
+    // keeps the scheduler from dequantising many operands ahead (they spill)
+    if constexpr (FMT == MOE_SCALE_E4M3_G16) __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Stable scan of the routing ids for expert e: the pairs p = t*K + j with
+// ids[p] == e, in increasing p, whose rank lies in [r0, r0 + kListCap), go to
+// list[rank - r0].  Returns the expert's total pair count.  All threads of
+// the workgroup call it.
+__device__ int collect_pairs(const int32_t* ids, int npairs, int e, int r0, int* list,
+                             int* wcnt) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int total = 0;
+  for (int base = 0; base < npairs; base += 64 * kBW) {
+    const int p = base + tid;
+    const bool m = p < npairs && ids[p] == e;
+    const uint64_t b = __ballot(m);
+    if (lane == 0) wcnt[wave] = __popcll(b);
+    __syncthreads();
+    int before = total;
+    for (int w = 0; w < wave; ++w) before += wcnt[w];
+    const int rank = before + __popcll(b & ((1ull << lane) - 1ull));
+    if (m && rank >= r0 && rank < r0 + kListCap) list[rank - r0] = p;
+    for (int w = 0; w < kBW; ++w) total += wcnt[w];
+    __syncthreads();
+  }
+  return total;
+}
+
+// Workgroup barrier for LDS data only.  __syncthreads() (and even an LDS-only
+// fence, because of the direct global->LDS loads) makes every wave wait for
+// all of its loads in flight, the weights included, at each barrier.  Here
+// each wave has already waited for its own direct loads (wait_vm below); the
+// barrier adds the wait for its LDS stores, and the empty asm statements keep
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4));  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Stage the 16 A rows of a pass into LDS with the gfx950 direct global->LDS
+// load: one wave instruction moves 1 KiB (16 bytes per lane, lane i at
+// base + 16 i); a row tail of 256 elements uses lanes 0..31.  Rows past the
+// pass's pair count are zero-filled with ordinary LDS stores.
+template <int MODE>
+__device__ __forceinline__ void stage_rows(const BatchedArgs& a, const int* lp, int mcnt, int Kd,
+                                           int ldx, uint16_t* xs, int wave, int lane) {
+  const int nch = (Kd + 511) / 512;
+  // Zero rows and the pair indices first: an LDS access between the direct
+  // loads would make the compiler wait for all of them.
+  for (int q = wave; q < kMC * nch; q += kBW) {
+    const int r = q / nch, ch = q - r * nch;
+    if (r >= mcnt && lane * 8 < Kd - ch * 512)
+      *(uint4*)(xs + r * ldx + ch * 512 + lane * 8) = make_uint4(0u, 0u, 0u, 0u);
+  }
+  const int mine = lp[lane < mcnt ? lane : 0];  // lane r < mcnt holds row r's pair
+  for (int q = wave; q < mcnt * nch; q += kBW) {
+    const int r = q / nch, ch = q - r * nch;
+    const int pair = __builtin_amdgcn_readlane(mine, r);
+    const uint16_t* src = (MODE == 0 ? a.x + (size_t)(pair / a.K) * Kd : a.hbuf + (size_t)pair * Kd) +
+                          ch * 512 + lane * 8;
+    if (lane * 8 < Kd - ch * 512)
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(xs + r * ldx + ch * 512),
+                                       16, 0, 0);
+  }
+}
+
+// One 16-token pass over staged A rows: optional RMS pre-norm (MODE 0), the
+// MFMAs over the whole contraction (blocks after the first are loaded here)
+// and the epilogue.  W holds the first block's steps on entry.
+template <int FMT, int MODE, int KB>
+__device__ __forceinline__ void gemm_pass(const BatchedArgs& a, WStep<FMT, (MODE == 0 ? 2 : 1)> (&W)[KB],
+                                          const uint8_t* const (&wrow)[2],
+                                          const uint8_t* const (&srow)[2], uint16_t* xs, int ldx,
+                                          const int* lp, int mcnt, int nkb, int n, int tile,
+                                          double tscale) {
+  constexpr int NMAT = MODE == 0 ? 2 : 1;
+  const int Kd = MODE == 0 ? a.H : a.I;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int ln = lane & 15, g = lane >> 4;
+  lds_barrier();  // every wave's A rows are in LDS
+  if (MODE == 0) {
+    const bool prenorm = (a.flags & MOE_FLAG_PRENORM) != 0;
+    for (int r = wave; r < mcnt; r += kBW) {
+      uint16_t* row = xs + r * ldx;
+      if (prenorm) {
+        double ss = 0.0;
+        for (int k = lane; k < Kd; k += 64) {
+          const double f = bf2f(row[k]);
+          ss += f * f;
+        }
+        ss = seg_finish<32, double>(ss, lane);
+        const double rs = 1.0 / sqrt(ss / (double)Kd + (double)a.eps);
+        for (int k = lane; k < Kd; k += 64) row[k] = f64_to_bf16((double)bf2f(row[k]) * rs);
+      }
+      if (a.du && tile == 0) {
+        const int t = lp[r] / a.K;
+        for (int k = lane; k < Kd; k += 64) a.du[(size_t)t * Kd + k] = row[k];
       }
     }
+    if (prenorm) lds_barrier();
+  }
+
+  double acc[2][4];
 #pragma unroll
-    for (int mt = 0; mt < NMAT; ++mt)
+  for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[mt][0][i] += (double)part[mt][0][i];
-        acc[mt][1][i] += (double)part[mt][1][i];
-      }
+    for (int i = 0; i < 4; ++i) acc[mt][i] = 0.0;
+  const uint16_t* arow = xs + ln * ldx + 64 * g;
+  for (int kb = 0; kb < nkb; ++kb) {
+    if (kb > 0) {
+#pragma unroll
+      for (int ks = 0; ks < KB; ++ks) load_wstep<FMT, NMAT>(W[ks], wrow, srow, kb * KB + ks, g);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KB; ++ks) wstep_mfma<FMT, NMAT>(W[ks], arow + (kb * KB + ks) * kKS, acc);
+  }
+
+  // epilogue: lane holds D[m = 4g + i][n] of the M tile
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = 4 * g + i;
+    if (m >= mcnt) continue;
+    const int pair = lp[m];
+    if (MODE == 0) {
+      const uint16_t gb = f64_to_bf16(acc[0][i] * tscale);
+      const uint16_t ub = f64_to_bf16(acc[1][i] * tscale);
+      const uint16_t h = silu_mul_bf16(gb, ub);
+      const size_t o = (size_t)pair * a.I + n;
+      a.hbuf[o] = h;
+      if (a.dg) a.dg[o] = gb;
+      if (a.dv) a.dv[o] = ub;
+      if (a.dh) a.dh[o] = h;
+    } else {
+      const uint16_t y = f64_to_bf16(acc[0][i] * tscale);
+      const size_t o = (size_t)pair * a.H + n;
+      a.ybuf[o] = y;
+      if (a.dy) a.dy[o] = y;
+    }
   }
 }
 
 // MODE 0: A = x rows (pre-normed if asked), B = gate and up -> h.
-// MODE 1: A = h rows, B = down -> y.
-template <int FMT, int MODE>
-__global__ __launch_bounds__(kBT) void k_bat_gemm(BatchedArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+// MODE 1: A = h rows, B = down -> y.   KB = K steps held in registers; when
+// they do not cover the contraction, blocks of KB steps follow in turn.
+template <int FMT, int MODE, int KB>
+__global__ __launch_bounds__(64 * kBW, 2) void k_bat_gemm(BatchedArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   constexpr int NMAT = MODE == 0 ? 2 : 1;
   constexpr int G = FMT == MOE_SCALE_E4M3_G16 ? 16 : 32;
   const int Kd = MODE == 0 ? a.H : a.I;
   const int Nd = MODE == 0 ? a.I : a.H;
   const int ntiles = Nd / kBN;
-  const int ai = blockIdx.x / ntiles, tile = blockIdx.x % ntiles;
-  if (ai >= *a.nactive) return;
-  const int e = a.active[ai];
-  const int M = a.counts[e], off = a.offsets[e];
+  const int e = blockIdx.x / ntiles, tile = blockIdx.x % ntiles;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ln = lane & 15, g = lane >> 4;
   const int n = tile * kBN + wave * 16 + ln;  // this lane's output row (B column)
   const int ldx = Kd + 8;                     // +16 B per row: conflict-free A reads
-
+  uint16_t* xs = lds;                         // [kMC][ldx]
+  int* list = (int*)(lds + kMC * ldx);        // [kListCap]
+  int* wcnt = list + kListCap;                 // [kBW]
+  const int npairs = a.T * a.K;
+  // Read before any store so that they become scalar loads: a vector load
+  // still in flight when the direct LDS loads below are issued would make
+  // the compiler wait for every one of those before the weight loads.
   const uint8_t* wb = a.wtab[e];
   const uint8_t* sb = a.stab[e];
-  const bool aligned = ((((uintptr_t)wb) | ((uintptr_t)sb)) & 15u) == 0;
-  if ((a.flags & MOE_FLAG_CHECK_IDS) && !aligned) {
+  double tscale = 1.0;
+  if constexpr (FMT == MOE_SCALE_E4M3_G16) tscale = (double)a.tsc[2 * e + MODE];
+
+  // 1. this expert's pairs (ids outside [0, E) match no expert: their y
+  //    stays as the caller cleared it; one workgroup reports them)
+  if (MODE == 0 && blockIdx.x == 0 && (a.flags & MOE_FLAG_CHECK_IDS)) {
+    bool bad = false;
+    for (int p = tid; p < npairs; p += 64 * kBW) bad |= (unsigned)a.ids[p] >= (unsigned)a.E;
+    if (bad) atomicOr(a.err, kErrBadId);
+  }
+  const int M = collect_pairs(a.ids, npairs, e, 0, list, wcnt);
+  if (M == 0) return;
+
+  if ((a.flags & MOE_FLAG_CHECK_IDS) && ((((uintptr_t)wb) | ((uintptr_t)sb)) & 15u)) {
     if (tid == 0) atomicOr(a.err, kErrAlign);
-    return;
+    return;  // its pairs keep y = 0 (the caller clears y under this flag)
   }
   const size_t rowb = (size_t)Kd / 2, rows = (size_t)Kd / G;
   const uint8_t* wrow[2];
@@ -208,90 +367,36 @@ __global__ __launch_bounds__(kBT) void k_bat_gemm(BatchedArgs a) {
     wrow[0] = wrow[1] = wb + (size_t)a.I * a.H + n * rowb;
     srow[0] = srow[1] = sb + 2 * (size_t)a.I * (a.H / G) + n * rows;
   }
-  double tscale = 1.0;
-  if constexpr (FMT == MOE_SCALE_E4M3_G16) tscale = (double)a.tsc[2 * e + MODE];
-  const int nks = Kd / kKS;
+  const int nkb = Kd / (kKS * KB);
 
-  for (int mc0 = 0; mc0 < M; mc0 += a.mc) {
-    const int mcnt = min(a.mc, M - mc0);
-    __syncthreads();
-    // stage the chunk's A rows (zero rows pad the last M tile)
-    const int k8s = Kd / 8;
-    for (int idx = tid; idx < a.mc * k8s; idx += kBT) {
-      const int r = idx / k8s, k8 = idx - r * k8s;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (r < mcnt) {
-        const int pair = a.perm[off + mc0 + r];
-        const uint16_t* src = MODE == 0 ? a.x + (size_t)(pair / a.K) * Kd : a.hbuf + (size_t)pair * Kd;
-        v = ldg16(src + 8 * k8);
-      }
-      *(uint4*)(xs + r * ldx + 8 * k8) = v;
-    }
-    __syncthreads();
-    if (MODE == 0) {
-      const bool prenorm = (a.flags & MOE_FLAG_PRENORM) != 0;
-      for (int r = wave; r < mcnt; r += kBT / 64) {
-        uint16_t* row = xs + r * ldx;
-        if (prenorm) {
-          double ss = 0.0;
-          for (int k = lane; k < Kd; k += 64) {
-            const double f = bf2f(row[k]);
-            ss += f * f;
-          }
-          ss = seg_finish<32, double>(ss, lane);
-          const double den = sqrt(ss / (double)Kd + (double)a.eps);
-          for (int k = lane; k < Kd; k += 64) row[k] = f64_to_bf16((double)bf2f(row[k]) / den);
-        }
-        if (a.du && tile == 0) {
-          const int t = a.perm[off + mc0 + r] / a.K;
-          for (int k = lane; k < Kd; k += 64) a.du[(size_t)t * Kd + k] = row[k];
-        }
-      }
-      if (prenorm) __syncthreads();
-    }
-
-    double acc[2][2][4];
+  // 2. per 16-token pass: the A rows go straight from global memory (L2) into
+  //    LDS, then the first KB steps of weights are issued; loads retire in
+  //    issue order, so the wait for this wave's A rows leaves the weight loads
+  //    in flight.  The first pass is peeled off the loop: with the weight loads
+  //    outside a loop nothing computed from them is hoisted ahead of the A
+  //    staging (which would wait for them).  Later passes (experts with more
+  //    than 16 tokens) re-read the weights, from L2.
+  WStep<FMT, NMAT> W[KB];
+  int mcnt = min(kMC, M);
+  stage_rows<MODE>(a, list, mcnt, Kd, ldx, xs, wave, lane);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+  for (int ks = 0; ks < KB; ++ks) load_wstep<FMT, NMAT>(W[ks], wrow, srow, ks, g);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vm<3 * KB * NMAT>();
+  gemm_pass<FMT, MODE, KB>(a, W, wrow, srow, xs, ldx, list, mcnt, nkb, n, tile, tscale);
+  for (int c0 = kMC; c0 < M; c0 += kMC) {
+    lds_barrier();  // the previous pass has read xs and its pair indices
+    if (c0 % kListCap == 0) collect_pairs(a.ids, npairs, e, c0, list, wcnt);
+    const int* lp = list + (c0 % kListCap);
+    mcnt = min(kMC, M - c0);
+    stage_rows<MODE>(a, lp, mcnt, Kd, ldx, xs, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mt][q][i] = 0.0;
-    const bool two = mcnt > 16;
-    Step cur, nxt;
-    load_step<FMT, NMAT>(cur, wrow, srow, 0, g);
-    nxt = cur;
-    for (int ks = 0; ks < nks; ++ks) {
-      if (ks + 1 < nks) load_step<FMT, NMAT>(nxt, wrow, srow, ks + 1, g);
-      step_mfma<FMT, NMAT>(cur, xs, ldx, ks, ln, g, two, acc);
-      cur = nxt;
-    }
-
-    // epilogue: lane holds D[m = 4g + i][n] of each M tile
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 16 * q + 4 * g + i;
-        if (m >= mcnt) continue;
-        const int pair = a.perm[off + mc0 + m];
-        if (MODE == 0) {
-          const uint16_t gb = f64_to_bf16(acc[0][q][i] * tscale);
-          const uint16_t ub = f64_to_bf16(acc[1][q][i] * tscale);
-          const uint16_t h = silu_mul_bf16(gb, ub);
-          const size_t o = (size_t)pair * a.I + n;
-          a.hbuf[o] = h;
-          if (a.dg) a.dg[o] = gb;
-          if (a.dv) a.dv[o] = ub;
-          if (a.dh) a.dh[o] = h;
-        } else {
-          const uint16_t y = f64_to_bf16(acc[0][q][i] * tscale);
-          const size_t o = (size_t)pair * a.H + n;
-          a.ybuf[o] = y;
-          if (a.dy) a.dy[o] = y;
-        }
-      }
-    }
+    for (int ks = 0; ks < KB; ++ks) load_wstep<FMT, NMAT>(W[ks], wrow, srow, ks, g);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<3 * KB * NMAT>();
+    gemm_pass<FMT, MODE, KB>(a, W, wrow, srow, xs, ldx, lp, mcnt, nkb, n, tile, tscale);
   }
 }
 
@@ -339,21 +444,48 @@ hipError_t allow_lds(KernelT kernel, size_t bytes) {
                              (int)bytes);
 }
 
+template <int FMT, int MODE, int KB>
+hipError_t launch_gemm_kb(const BatchedArgs& a, hipStream_t s) {
+  const int Kd = MODE == 0 ? a.H : a.I, Nd = MODE == 0 ? a.I : a.H;
+  const size_t lds = (size_t)kMC * (Kd + 8) * 2 + (size_t)(kListCap + kBW) * 4;
+  // The largest contraction a shape check admits (4096) needs 136.3 KiB.
+  static size_t allowed = 0;  // benign race: the value only grows towards the same bound
+  if (lds > allowed) {
+    hipError_t e = allow_lds(k_bat_gemm<FMT, MODE, KB>, lds);
+    if (e != hipSuccess) return e;
+    allowed = lds;
+  }
+  k_bat_gemm<FMT, MODE, KB><<<a.E * (Nd / kBN), 64 * kBW, lds, s>>>(a);
+  return hipGetLastError();
+}
+
+// Up to 8 K steps (2048 contraction elements) stay in registers for the whole
+// call; longer contractions go in blocks of 8, 4, 2 or 1 steps.
+template <int FMT, int MODE>
+hipError_t launch_gemm(const BatchedArgs& a, hipStream_t s) {
+  const int nks = (MODE == 0 ? a.H : a.I) / kKS;
+  switch (nks) {
+    case 1: return launch_gemm_kb<FMT, MODE, 1>(a, s);
+    case 2: return launch_gemm_kb<FMT, MODE, 2>(a, s);
+    case 3: return launch_gemm_kb<FMT, MODE, 3>(a, s);
+    case 4: return launch_gemm_kb<FMT, MODE, 4>(a, s);
+    case 5: return launch_gemm_kb<FMT, MODE, 5>(a, s);
+    case 6: return launch_gemm_kb<FMT, MODE, 6>(a, s);
+    case 7: return launch_gemm_kb<FMT, MODE, 7>(a, s);
+    case 8: return launch_gemm_kb<FMT, MODE, 8>(a, s);
+    default: break;
+  }
+  if (nks % 8 == 0) return launch_gemm_kb<FMT, MODE, 8>(a, s);
+  if (nks % 4 == 0) return launch_gemm_kb<FMT, MODE, 4>(a, s);
+  if (nks % 2 == 0) return launch_gemm_kb<FMT, MODE, 2>(a, s);
+  return launch_gemm_kb<FMT, MODE, 1>(a, s);
+}
+
 template <int FMT>
 hipError_t launch_batched_fmt(const BatchedArgs& a, hipStream_t s) {
-  hipError_t err = launch_sort(a.ids, a.T * a.K, a.E, a.counts, a.offsets, a.perm, a.active,
-                               a.nactive, a.err, a.flags, s);
+  hipError_t err = launch_gemm<FMT, 0>(a, s);
   if (err != hipSuccess) return err;
-  const size_t lds0 = (size_t)a.mc * (a.H + 8) * 2, lds1 = (size_t)a.mc * (a.I + 8) * 2;
-  static bool attrs_set = false;  // benign race: every caller sets the same values
-  if (!attrs_set) {
-    if ((err = allow_lds(k_bat_gemm<FMT, 0>, 160 * 1024)) != hipSuccess) return err;
-    if ((err = allow_lds(k_bat_gemm<FMT, 1>, 160 * 1024)) != hipSuccess) return err;
-    attrs_set = true;
-  }
-  k_bat_gemm<FMT, 0><<<a.E * (a.I / kBN), kBT, lds0, s>>>(a);
-  k_bat_gemm<FMT, 1><<<a.E * (a.H / kBN), kBT, lds1, s>>>(a);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if ((err = launch_gemm<FMT, 1>(a, s)) != hipSuccess) return err;
   return launch_combine(a.ybuf, a.rw, a.residual, a.out, a.T, a.K, a.H, s);
 }
 
@@ -361,11 +493,6 @@ hipError_t launch_batched_fmt(const BatchedArgs& a, hipStream_t s) {
 
 bool batched_supported(int H, int I) {
   return H > 0 && I > 0 && H % kKS == 0 && I % kKS == 0 && H <= 4096 && I <= 4096;
-}
-
-int batched_chunk_tokens(int H, int I) {
-  const int kmax = H > I ? H : I;
-  return (size_t)32 * (kmax + 8) * 2 <= 160 * 1024 ? 32 : 16;
 }
 
 hipError_t launch_sort(const int32_t* ids, int npairs, int E, int32_t* counts, int32_t* offsets,

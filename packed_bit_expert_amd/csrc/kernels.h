@@ -48,24 +48,17 @@ struct BatchedArgs {
   const float* tsc;
   const uint16_t* residual;
   uint16_t* out;
-  int32_t* counts;    // [E]
-  int32_t* offsets;   // [E + 1]
-  int32_t* active;    // [E] experts with at least one pair, in id order
-  int32_t* nactive;   // [1]
-  int32_t* perm;      // [T * K]
   uint16_t* hbuf;     // [T * K][I]
   uint16_t* ybuf;     // [T * K][H]
   uint16_t *du, *dg, *dv, *dh, *dy;
   int* err;
   int T, H, I, K, E;
-  int mc;             // tokens per LDS chunk (16 or 32)
   uint32_t flags;
   float eps;
 };
 
 bool decode_supported(int H, int I);
 bool batched_supported(int H, int I);
-int batched_chunk_tokens(int H, int I);
 
 hipError_t launch_decode(const DecodeArgs& a, int fmt, hipStream_t s);
 // Resolve n = L*T*K slots of consecutive layers: out[i] for ids[i] of layer
