@@ -40,11 +40,19 @@ def parse():
                    help="also run a 1 GiB stream read and a 256 MiB copy (counter calibration)")
     p.add_argument("--eager", action="store_true",
                    help="launch every step from the host instead of replaying a captured HIP graph")
+    p.add_argument("--timing-steps", type=int, default=16,
+                   help="steps of the per-kernel event timing pass (0 = skip)")
+    p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                        "`bench.py --calib` into profiles/ and exit")
     return p.parse_args()
 
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(expert-parallel sharding is a design note, not code). Use --gpus 1.", file=sys.stderr)
@@ -134,44 +142,98 @@ def main():
     ms_step = ms / args.steps
 
     # algorithmic bytes: each call reads its distinct selected experts' packed
-    # bytes once (+ activations in/out, negligible)
-    eb = shape.expert_bytes(w.fmt)
+    # bytes once, plus activations in and out
     ids_h = ids[args.warmup:].cpu().numpy()
     if stack:
-        distinct = sum(len(np.unique(ids_h[s, l])) for s in range(args.steps) for l in range(L))
-        layer_calls = args.steps * L
+        distinct = [len(np.unique(ids_h[s, l])) for s in range(args.steps) for l in range(L)]
     else:
-        distinct = sum(len(np.unique(ids_h[s])) for s in range(args.steps))
-        layer_calls = args.steps
-    alg_bytes = distinct * eb + layer_calls * 2 * T * H * 2
+        distinct = [len(np.unique(ids_h[s])) for s in range(args.steps)]
+    layer_calls = len(distinct)
+    act = T * H * 2
+    per_kind = kernel_bytes(shape, w, T, float(np.mean(distinct)), chained=w.chained)
+    alg_bytes = sum(distinct) * shape.expert_bytes(w.fmt) + layer_calls * act * (3 if w.chained else 2)
     secs = ms / 1e3
-    achieved = alg_bytes / secs / 1e9
+    achieved_step = alg_bytes / secs / 1e9
     tok_layer_per_s = T * layer_calls / secs
 
+    # per-kernel durations: HIP events on the launch stream around every
+    # launch, the same steps replayed eagerly behind a delay kernel so that
+    # the queue is full and each event pair brackets only its kernel
+    kernels = []
+    dominant = None
+    if args.timing_steps > 0:
+        nt = min(args.timing_steps, args.steps)
+        chunk = 4 if stack else 64
+        cap = 4096
+        durs = {}
+        for c0 in range(0, nt, chunk):
+            M.moe_w4a16_delay(30000, stream)
+            M.moe_w4a16_timing_begin(cap)
+            for s in range(args.warmup + c0, args.warmup + min(nt, c0 + chunk)):
+                step(s)
+            msl, kinds = M.moe_w4a16_timing_end(cap)
+            for d, k in zip(msl, kinds):
+                durs.setdefault(k, []).append(d)
+        torch.cuda.synchronize()
+        for k, v in sorted(durs.items()):
+            v = np.array(v)
+            rec = {"kernel": M.KERNEL_KINDS.get(k, str(k)), "launches_per_step": len(v) / nt,
+                   "mean_us": float(v.mean() * 1e3), "median_us": float(np.median(v) * 1e3),
+                   "min_us": float(v.min() * 1e3), "share_of_kernel_time": None}
+            if k in per_kind:
+                rec["alg_bytes_per_launch"] = per_kind[k]
+                rec["achieved_GBps"] = per_kind[k] / (v.mean() / 1e3) / 1e9
+            rec["_kind"] = k
+            rec["_total"] = float(v.sum())
+            kernels.append(rec)
+        tot = sum(r["_total"] for r in kernels)
+        for r in kernels:
+            r["share_of_kernel_time"] = r["_total"] / tot
+        dominant = max(kernels, key=lambda r: r["_total"])
+
     # achievable HBM read bandwidth on this GPU (16-byte loads over 1 GiB)
-    if True:
-        buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        sink = torch.empty(4096, dtype=torch.int32, device=dev)
-        for _ in range(2):
-            M.moe_w4a16_stream_read(buf, buf.numel(), sink, stream)
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.empty(4096, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        M.moe_w4a16_stream_read(buf, buf.numel(), sink, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        M.moe_w4a16_stream_read(buf, buf.numel(), sink, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    stream_gbps = 5 * buf.numel() / (e0.elapsed_time(e1) / 1e3) / 1e9
+    if args.calib:
+        # counter calibration: one more 1 GiB read and a 256 MiB device copy
+        M.moe_w4a16_stream_read(buf, buf.numel(), sink, stream)
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(5):
-            M.moe_w4a16_stream_read(buf, buf.numel(), sink, stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        stream_gbps = 5 * buf.numel() / (e0.elapsed_time(e1) / 1e3) / 1e9
-        if args.calib:
-            src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-            dst = torch.empty_like(src)
-            dst.copy_(src)
-            torch.cuda.synchronize()
-        del buf
+    del buf
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, shape, args.cpu_seconds)
+
+    if dominant is not None and "achieved_GBps" in dominant:
+        roof = {"bound": "hbm", "achieved": dominant["achieved_GBps"], "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": dominant["achieved_GBps"] / HBM_PEAK_GBPS,
+                "traffic": traffic_for(dominant["_kind"], args.workload),
+                "kernel": dominant["kernel"],
+                "alg_bytes_per_launch": dominant["alg_bytes_per_launch"],
+                "mean_launch_us": dominant["mean_us"]}
+        if dominant["_kind"] in (4, 5):
+            fl = kernel_flops(shape, T, dominant["_kind"])
+            roof["mfma_useful_TFLOPs"] = fl / (dominant["mean_us"] / 1e6) / 1e12
+            roof["mfma_useful_frac_of_bf16_peak"] = roof["mfma_useful_TFLOPs"] / 2500.0
+    else:
+        roof = {"bound": "hbm", "achieved": achieved_step, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved_step / HBM_PEAK_GBPS, "traffic": None, "kernel": "whole step"}
+    for r in kernels:
+        r.pop("_kind")
+        r.pop("_total")
 
     res = {
         "metric": "MoE-layer tokens/s & achieved HBM GB/s (% of peak), 24B-A2B shape, batch 1/32",
@@ -193,17 +255,125 @@ def main():
             "weights": "E2M1 + E4M3/16 + FP32 tensor scale" if w.fmt else "E2M1 + E8M0/32",
             "stack_tokens_per_s": T * args.steps / secs if stack else None,
             "graph_replay": not args.eager,
-        },
-        "roofline": {
-            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-            "kernel": "whole step (all MoE kernels of the step)",
+            "step_achieved_GBps": achieved_step,
+            "step_frac_of_peak": achieved_step / HBM_PEAK_GBPS,
             "algorithmic_bytes_per_step": alg_bytes / args.steps,
         },
+        "roofline": roof,
+        "kernels": kernels,
         "hbm_stream_read_GBps": stream_gbps,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def kernel_bytes(shape, w, T, distinct, chained):
+    """Algorithmic bytes per launch of each kernel kind: the packed weights and
+    scales of the distinct selected experts that kernel reads, plus the
+    activations it reads or writes in HBM by definition (x in; out and the
+    residual).  Intermediates (h, y) are not counted."""
+    H, I = shape.hidden, shape.inter
+    G = shape.group(w.fmt)
+    gu = 2 * I * (H // 2 + H // G)
+    dn = H * (I // 2 + I // G)
+    act = T * H * 2
+    return {1: distinct * gu + act, 2: distinct * dn + act * (2 if chained else 1),
+            4: distinct * gu + act, 5: distinct * dn, 6: act * (2 if chained else 1)}
+
+
+def kernel_flops(shape, T, kind):
+    H, I, K = shape.hidden, shape.inter, shape.top_k
+    return 2 * T * K * (2 * I * H if kind == 4 else H * I)
+
+
+def source_hash(kind):
+    import hashlib
+    files = {1: "decode.hip", 2: "decode.hip", 4: "batched.hip", 5: "batched.hip", 6: "batched.hip"}
+    h = hashlib.sha256()
+    for f in (files.get(kind, "api.hip"), "common.h"):
+        with open(os.path.join(ROOT, "packed_bit_expert_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KIND_FILE = {1: "dec_gateup", 2: "dec_down", 4: "bat_gateup", 5: "bat_down", 6: "combine"}
+TRAFFIC_FILE = "hbm_traffic_{kind}_{workload}.txt"
+
+
+def traffic_for(kind, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this kernel and workload, or None if there is none or the kernel source
+    changed since the counters were taken."""
+    if kind not in KIND_FILE:
+        return None
+    p = os.path.join(ROOT, "profiles", TRAFFIC_FILE.format(kind=KIND_FILE[kind], workload=workload))
+    if not os.path.exists(p):
+        return None
+    kv = {}
+    for line in open(p):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_hash(kind):
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
+def pmc_summary(args):
+    """Read rocprofv3 counter CSVs of `bench.py --calib` runs (one with
+    FETCH_SIZE, one with WRITE_SIZE), scale each counter by what it reads for
+    the calibration kernels of known size (1 GiB stream read, 256 MiB copy),
+    and write per-kernel HBM bytes per launch to profiles/."""
+    import csv
+    import glob
+
+    def load(d, counter):
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+        if not rows:
+            sys.exit(f"no {counter} rows under {d}")
+        return rows
+
+    fetch = load(args.pmc_summary[0], "FETCH_SIZE")
+    write = load(args.pmc_summary[1], "WRITE_SIZE")
+
+    def per_kernel(rows, pat):
+        v = [x for n, x in rows if pat in n]
+        return (sum(v) / len(v), len(v)) if v else (None, 0)
+
+    gib_kib = float(1 << 20)
+    sr, _ = per_kernel(fetch, "k_stream_read")
+    cp_w, _ = per_kernel(write, "copyBuffer")
+    if cp_w is None:
+        cp_w, _ = per_kernel(write, "elementwise")
+    f_fetch = gib_kib / max(v for n, v in fetch if "k_stream_read" in n)
+    f_write = (256 * 1024.0) / max(v for n, v in write if ("copyBuffer" in n or "elementwise" in n))
+    names = {1: "k_dec_gateup", 2: "k_dec_down", 4: "k_bat_gemm<0, 0", 5: "k_bat_gemm<0, 1"}
+    wl = os.environ.get("PMC_WORKLOAD", "c1")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    for kind, pat in names.items():
+        fk, nf = per_kernel(fetch, pat)
+        wk, nw = per_kernel(write, pat)
+        if fk is None or wk is None:
+            continue
+        hbm = (fk * f_fetch + wk * f_write) * 1024.0
+        p = os.path.join(ROOT, "profiles", TRAFFIC_FILE.format(kind=KIND_FILE[kind], workload=wl))
+        with open(p, "w") as fh:
+            fh.write(f"# HBM traffic per launch of {pat}* ({wl}), from rocprofv3 --pmc FETCH_SIZE and\n"
+                     f"# WRITE_SIZE runs of: {os.environ.get('PMC_COMMAND', 'bench.py --calib')}\n"
+                     f"# counters scaled by their reading for kernels of known size: FETCH_SIZE of\n"
+                     f"# the 1 GiB stream read, WRITE_SIZE of the 256 MiB device copy\n")
+            fh.write(f"kernel: {pat}\nworkload: {wl}\n")
+            fh.write(f"dispatches_fetch: {nf}\ndispatches_write: {nw}\n")
+            fh.write(f"fetch_kib_per_launch_raw: {fk:.1f}\nwrite_kib_per_launch_raw: {wk:.1f}\n")
+            fh.write(f"fetch_factor: {f_fetch:.4f}\nwrite_factor: {f_write:.4f}\n")
+            fh.write(f"calib_stream_read_fetch_kib: {1 / f_fetch * gib_kib:.1f}\n")
+            fh.write(f"hbm_bytes_per_launch: {hbm:.0f}\n")
+            fh.write(f"source_sha256: {source_hash(kind)}\n")
+        print(open(p).read())
 
 
 def workload_name(k):
@@ -219,41 +389,46 @@ def workload_name(k):
 
 
 def cpu_baseline(w, shape, target_s):
-    """The oracle as it stands on this host's cores, on a bounded sample: one
-    token (or one call of the workload's batch) through consecutive layers
-    until about `target_s` seconds of wall time have passed."""
+    """The oracle as it stands on this host's cores, on a bounded sample of the
+    workload: layer calls of the workload's batch in the workload's order
+    (consecutive layers of one step, chained through the pre-norm and residual
+    for the stack), until about `target_s` seconds of oracle time."""
     import numpy as np
 
     from oracle import oracle as O
     from packed_bit_expert_amd import synth as S
     threads = O.threads_available()
     T = w.tokens
-    t0 = time.time()
-    layers = 0
-    tokens = 0
-    h = S.activations(w.family, 0, 10_000, T, shape.hidden)
-    gen_time = 0.0
-    while time.time() - t0 - gen_time < target_s and layers < shape.layers:
-        g0 = time.time()
-        ids, rw = S.routing(w, layers, 10_000)
+    busy = 0.0
+    calls = 0
+    h = None
+    while busy < target_s:
+        layer, step = calls % shape.layers, 10_000 + calls // shape.layers
+        if w.chained:
+            if layer == 0:
+                h = S.activations(w.family, 0, step, T, shape.hidden)
+        else:
+            h = S.activations(w.family, layer, step, T, shape.hidden)
+        ids, rw = S.routing(w, layer, step)
         nib = [None] * shape.experts
         sc = [None] * shape.experts
         for e in np.unique(ids):
-            nib[int(e)] = S.expert_nibbles(shape, w.fmt, layers, int(e))
-            sc[int(e)] = S.expert_scales(shape, w.fmt, layers, int(e))
-        ts = S.tensor_scales(shape, w.fmt, layers)
-        gen_time += time.time() - g0
+            nib[int(e)] = S.expert_nibbles(shape, w.fmt, layer, int(e))
+            sc[int(e)] = S.expert_scales(shape, w.fmt, layer, int(e))
+        ts = S.tensor_scales(shape, w.fmt, layer)
+        t0 = time.perf_counter()
         out = O.moe_forward(h, ids, rw, nib, sc, hidden=shape.hidden, inter=shape.inter,
                             num_experts=shape.experts, fmt=w.fmt, tensor_scales=ts,
                             residual=h if w.chained else None, prenorm=w.chained, eps=EPS)
-        h = out if w.chained else h
-        layers += 1
-        tokens += T
-    wall = time.time() - t0 - gen_time
-    return {"value": tokens / wall, "unit": "tokens/s per MoE layer", "cores": threads,
+        busy += time.perf_counter() - t0
+        if w.chained:
+            h = out
+        calls += 1
+    return {"value": T * calls / busy, "unit": "tokens/s per MoE layer", "cores": threads,
             "kind": "oracle",
-            "sample": f"{layers} layer calls of {T} token(s) ({w.name} inputs), fp64 scalar oracle, "
-                      f"{threads} OpenMP threads, {wall:.1f} s (input generation excluded)"}
+            "sample": f"{calls} layer calls of {T} token(s) on {w.name} inputs (layers 0..{min(calls, shape.layers) - 1}"
+                      f"{', chained' if w.chained else ''}), fp64 scalar C oracle with {threads} OpenMP "
+                      f"threads, {busy:.1f} s of oracle time (input generation excluded)"}
 
 
 if __name__ == "__main__":

@@ -149,9 +149,10 @@ int moe_w4a16_workspace_init(void* workspace, size_t bytes, void* stream);
  *   route_w    device BF16 [T][k] routing coefficients
  *   packed_weights, scales   device tables [E] of device pointers (layout above)
  *   out        device BF16 [T][H], 16-byte aligned, must not overlap x
- * T = 1 uses the one-launch decode kernel; T > 1 uses the sorted batched
- * path (device-side stable sort of the (token, slot) pairs by expert, then
- * grouped BF16-MFMA GEMMs on LDS-dequantised tiles, then the combine).
+ * T = 1 uses the decode path (one gate/up GEMV launch for all k experts,
+ * then one down GEMV launch that also does the combine); T > 1 uses the
+ * batched path (grouped BF16-MFMA GEMMs whose workgroups group the
+ * (token, slot) pairs by expert on the device, then the combine).
  */
 int moe_w4a16_forward(const void* x, const int32_t* expert_ids, const void* route_w,
                       const void* const* packed_weights, const void* const* scales,
@@ -175,8 +176,9 @@ int moe_w4a16_forward_debug(const void* x, const int32_t* expert_ids, const void
  *   expert_ids  device int32 [L][T][k]; route_w device BF16 [L][T][k]
  *   packed_weights, scales   device tables [L][E]
  *   tensor_scales            device FP32 [L][E][2] (E4M3) or NULL (E8M0)
- * At T = 1 the whole stack is one kernel launch; otherwise one batched
- * sequence per layer.
+ * At T = 1 every layer is two decode launches (the routing slots of up to 64
+ * layers are resolved to expert addresses by one extra launch); otherwise
+ * each layer is one batched sequence.
  */
 int moe_w4a16_stack_forward(int32_t num_layers, const void* x, const int32_t* expert_ids,
                             const void* route_w, const void* const* packed_weights,
@@ -230,6 +232,40 @@ int moe_w4a16_device_status(void* workspace, int32_t* host_code, void* stream);
  * workgroup to `sink` (device, 4 * 4096 bytes), to measure the achievable
  * HBM read bandwidth next to the kernels above. */
 int moe_w4a16_stream_read(const void* src, size_t bytes, void* sink, void* stream);
+
+/* Measurement helper: one wave that spins for `microseconds` (at most
+ * 1,000,000) on the 100 MHz real-time counter, so that a host can enqueue
+ * work behind it and the GPU then runs that work back to back. */
+int moe_w4a16_delay(uint32_t microseconds, void* stream);
+
+/* Kernel kinds reported by moe_w4a16_timing_end. */
+#define MOE_KERNEL_DECODE_GATE_UP 1  /* decode: gate/up GEMV + SiLU*up, all k slots */
+#define MOE_KERNEL_DECODE_DOWN 2     /* decode: down GEMV + combine (+ residual) */
+#define MOE_KERNEL_RESOLVE 3         /* routing slots -> expert addresses */
+#define MOE_KERNEL_BATCHED_GATE_UP 4 /* batched: grouped gate/up GEMM + SiLU*up */
+#define MOE_KERNEL_BATCHED_DOWN 5    /* batched: grouped down GEMM */
+#define MOE_KERNEL_COMBINE 6         /* slot-order combine (+ residual) */
+#define MOE_KERNEL_SORT 7            /* moe_w4a16_sort_pairs */
+#define MOE_KERNEL_DEQUANT 8         /* moe_w4a16_dequant */
+#define MOE_KERNEL_STREAM_READ 9     /* moe_w4a16_stream_read */
+#define MOE_KERNEL_ZERO 10           /* workspace fill */
+#define MOE_KERNEL_DELAY 11          /* moe_w4a16_delay */
+
+/*
+ * Kernel timing (measurement only).  After moe_w4a16_timing_begin(capacity)
+ * the calling thread's next `capacity` kernel launches of this library carry
+ * a start and a stop HIP event that the kernel dispatch itself records
+ * (hipExtLaunchKernel), so each pair spans exactly that kernel's execution
+ * (launches into a stream under graph capture carry none).  The library
+ * creates the events; moe_w4a16_timing_end waits for them, writes the
+ * duration in milliseconds and the MOE_KERNEL_* kind of each timed launch,
+ * in launch order, to the host arrays ms[] and kinds[] (room for `capacity`
+ * entries), destroys the events and returns the number of launches written,
+ * or a negative error (MOE_ERR_INVALID_ARG if more launches happened than
+ * the capacity, or if timing was not begun on this thread).
+ */
+int moe_w4a16_timing_begin(int32_t capacity);
+int moe_w4a16_timing_end(float* ms, int32_t* kinds, int32_t capacity);
 
 #ifdef __cplusplus
 }

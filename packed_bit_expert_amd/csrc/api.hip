@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <vector>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -38,6 +40,21 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
   return na && nb && x < y + nb && y < x + na;
+}
+
+// Kernel timing state of the calling thread (moe_w4a16_timing_*).
+struct Timing {
+  std::vector<hipEvent_t> ev;  // two per launch
+  std::vector<int32_t> kind;
+  int n = 0;          // launches recorded
+  bool on = false;
+  bool overflow = false;
+};
+thread_local Timing g_timing;
+
+bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(s, &st) == hipSuccess && st != hipStreamCaptureStatusNone;
 }
 
 // Workspace regions (offsets from the base, each 256-byte aligned).
@@ -379,3 +396,88 @@ int moe_w4a16_stream_read(const void* src, size_t bytes, void* sink, void* strea
 }
 
 }  // extern "C"
+
+namespace moe {
+
+LaunchEvents timing_begin(int kind, hipStream_t s) {
+  Timing& t = g_timing;
+  LaunchEvents ev;
+  if (!t.on || capturing(s)) return ev;
+  if (t.n >= (int)t.kind.size()) {
+    t.overflow = true;
+    return ev;
+  }
+  t.kind[t.n] = kind;
+  ev.start = t.ev[2 * t.n];
+  ev.stop = t.ev[2 * t.n + 1];
+  return ev;
+}
+
+void timing_end(const LaunchEvents& ev) {
+  if (ev.start) ++g_timing.n;
+}
+
+}  // namespace moe
+
+namespace {
+
+void timing_release() {
+  Timing& t = g_timing;
+  for (hipEvent_t e : t.ev) hipEventDestroy(e);
+  t = Timing();
+}
+
+}  // namespace
+
+extern "C" int moe_w4a16_timing_begin(int32_t capacity) {
+  if (capacity < 1 || capacity > (1 << 20))
+    return fail(MOE_ERR_INVALID_ARG, "timing capacity %d outside 1..2^20", capacity);
+  timing_release();
+  Timing& t = g_timing;
+  t.ev.resize(2 * (size_t)capacity, nullptr);
+  for (auto& e : t.ev) {
+    const hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      timing_release();
+      return hip_fail(r, "hipEventCreate");
+    }
+  }
+  t.kind.assign(capacity, 0);
+  t.on = true;
+  return ok();
+}
+
+extern "C" int moe_w4a16_timing_end(float* ms, int32_t* kinds, int32_t capacity) {
+  Timing& t = g_timing;
+  if (!t.on) return fail(MOE_ERR_INVALID_ARG, "kernel timing was not begun on this thread");
+  if (t.overflow) {
+    timing_release();
+    return fail(MOE_ERR_INVALID_ARG, "more launches than the timing capacity");
+  }
+  if (!ms || !kinds || capacity < t.n) {
+    const int n = t.n;
+    timing_release();
+    return fail(MOE_ERR_INVALID_ARG, "output arrays missing or shorter than %d launches", n);
+  }
+  for (int i = 0; i < t.n; ++i) {
+    hipError_t r = hipEventSynchronize(t.ev[2 * i + 1]);
+    if (r == hipSuccess) r = hipEventElapsedTime(&ms[i], t.ev[2 * i], t.ev[2 * i + 1]);
+    if (r != hipSuccess) {
+      timing_release();
+      return hip_fail(r, "kernel timing events");
+    }
+    kinds[i] = t.kind[i];
+  }
+  const int n = t.n;
+  timing_release();
+  ok();
+  return n;
+}
+
+extern "C" int moe_w4a16_delay(uint32_t microseconds, void* stream) {
+  if (microseconds > 1000000u)
+    return fail(MOE_ERR_INVALID_ARG, "delay %u us above 1,000,000", microseconds);
+  const hipError_t e = launch_delay(microseconds, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "delay launch");
+  return ok();
+}

@@ -455,8 +455,8 @@ hipError_t launch_gemm_kb(const BatchedArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     allowed = lds;
   }
-  k_bat_gemm<FMT, MODE, KB><<<a.E * (Nd / kBN), 64 * kBW, lds, s>>>(a);
-  return hipGetLastError();
+  return launch_kernel(MODE == 0 ? MOE_KERNEL_BATCHED_GATE_UP : MOE_KERNEL_BATCHED_DOWN,
+                       k_bat_gemm<FMT, MODE, KB>, dim3(a.E * (Nd / kBN)), dim3(64 * kBW), lds, s, a);
 }
 
 // Up to 8 K steps (2048 contraction elements) stay in registers for the whole
@@ -498,17 +498,16 @@ bool batched_supported(int H, int I) {
 hipError_t launch_sort(const int32_t* ids, int npairs, int E, int32_t* counts, int32_t* offsets,
                        int32_t* perm, int32_t* active, int32_t* nactive, int* err, uint32_t flags,
                        hipStream_t s) {
-  k_sort<<<1, 256, (size_t)2 * E * sizeof(int32_t), s>>>(ids, npairs, E, counts, offsets, perm,
-                                                         active, nactive, err, flags);
-  return hipGetLastError();
+  return launch_kernel(MOE_KERNEL_SORT, k_sort, dim3(1), dim3(256), (size_t)2 * E * sizeof(int32_t), s,
+                       ids, npairs, E, counts, offsets, perm, active, nactive, err, flags);
 }
 
 hipError_t launch_combine(const uint16_t* y, const uint16_t* rw, const uint16_t* residual,
                           uint16_t* out, int T, int K, int H, hipStream_t s) {
   if (T == 0) return hipSuccess;
   dim3 grid((H / 8 + 255) / 256, T);
-  k_combine<<<grid, 256, 0, s>>>(y, rw, residual, out, K, H);
-  return hipGetLastError();
+  return launch_kernel(MOE_KERNEL_COMBINE, k_combine, grid, dim3(256), 0, s, y, rw, residual, out,
+                       K, H);
 }
 
 hipError_t launch_batched(const BatchedArgs& a, int fmt, hipStream_t s) {

@@ -364,9 +364,11 @@ hipError_t launch_variant(const DecodeArgs& a, hipStream_t s) {
   // to one token
   if (PRENORM && ((I / GuShape<H>::RW) * a.K) % 4 != 0) return hipErrorInvalidValue;
   const int waves = a.T * a.K * ((I + GuShape<H>::RW - 1) / GuShape<H>::RW);
-  k_dec_gateup<H, FMT, PRENORM, DUMP><<<(waves + 3) / 4, 256, 0, s>>>(a);
-  k_dec_down<H, I, FMT, DUMP><<<a.T * (H / DnShape<I>::ROWS), 256, 0, s>>>(a);
-  return hipGetLastError();
+  const hipError_t e = launch_kernel(MOE_KERNEL_DECODE_GATE_UP, k_dec_gateup<H, FMT, PRENORM, DUMP>,
+                                     dim3((waves + 3) / 4), dim3(256), 0, s, a);
+  if (e != hipSuccess) return e;
+  return launch_kernel(MOE_KERNEL_DECODE_DOWN, k_dec_down<H, I, FMT, DUMP>,
+                       dim3(a.T * (H / DnShape<I>::ROWS)), dim3(256), 0, s, a);
 }
 
 template <int H, int I, int FMT>
@@ -397,8 +399,9 @@ hipError_t launch_resolve(const int32_t* ids, const uint8_t* const* wtab,
                           const uint8_t* const* stab, const float* tsc, int n, int per_layer,
                           int E, uint32_t flags, int* err, SlotRef* out, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  k_resolve<<<(n + 255) / 256, 256, 0, s>>>(ids, wtab, stab, tsc, n, per_layer, E, flags, err, out);
-  return hipGetLastError();
+  const hipError_t e = launch_kernel(MOE_KERNEL_RESOLVE, k_resolve, dim3((n + 255) / 256), dim3(256),
+                                     0, s, ids, wtab, stab, tsc, n, per_layer, E, flags, err, out);
+  return e;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int fmt, hipStream_t s) {

@@ -1,6 +1,7 @@
 // Kernel launchers of the W4A16 MoE library (host side of the HIP kernels).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -76,5 +77,28 @@ hipError_t launch_dequant(const uint8_t* nib, const uint8_t* sc, int rows, int c
                           uint16_t* out, hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
+hipError_t launch_delay(uint32_t microseconds, hipStream_t s);
+
+// Kernel timing (moe_w4a16_timing_*): while the calling thread times
+// launches, each launch gets a start and a stop event that the dispatch
+// itself records (hipExtLaunchKernel), i.e. the kernel's own execution
+// interval; otherwise both are null and the launch is an ordinary one.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents timing_begin(int kind, hipStream_t s);
+void timing_end(const LaunchEvents& ev);
+
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(int kind, void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
+                         hipStream_t s, Args... args) {
+  const LaunchEvents ev = timing_begin(kind, s);
+  if (ev.start)
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)shmem, s, ev.start, ev.stop, 0u, args...);
+  else
+    kernel<<<grid, block, shmem, s>>>(args...);
+  timing_end(ev);
+  return hipGetLastError();
+}
 
 }  // namespace moe

@@ -54,6 +54,13 @@ __global__ __launch_bounds__(256) void k_stream_read(const uint4* __restrict__ s
   if (threadIdx.x == 0) sink[blockIdx.x] = red;
 }
 
+// One wave spinning on the 100 MHz real-time counter until `ticks` have
+// passed; the loop ends for any counter value, since the counter only grows.
+__global__ __launch_bounds__(64) void k_delay(uint64_t ticks) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (__builtin_amdgcn_s_memrealtime() - t0 < ticks) __builtin_amdgcn_s_sleep(16);
+}
+
 }  // namespace
 
 hipError_t launch_dequant(const uint8_t* nib, const uint8_t* sc, int rows, int cols, int fmt,
@@ -62,10 +69,10 @@ hipError_t launch_dequant(const uint8_t* nib, const uint8_t* sc, int rows, int c
   if (chunks == 0) return hipSuccess;
   const unsigned grid = (unsigned)((chunks + 255) / 256);
   if (fmt == MOE_SCALE_E4M3_G16)
-    k_dequant<MOE_SCALE_E4M3_G16><<<grid, 256, 0, s>>>(nib, sc, rows, cols, out);
-  else
-    k_dequant<MOE_SCALE_E8M0_G32><<<grid, 256, 0, s>>>(nib, sc, rows, cols, out);
-  return hipGetLastError();
+    return launch_kernel(MOE_KERNEL_DEQUANT, k_dequant<MOE_SCALE_E4M3_G16>, dim3(grid), dim3(256), 0,
+                         s, nib, sc, rows, cols, out);
+  return launch_kernel(MOE_KERNEL_DEQUANT, k_dequant<MOE_SCALE_E8M0_G32>, dim3(grid), dim3(256), 0, s,
+                       nib, sc, rows, cols, out);
 }
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
@@ -73,13 +80,18 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
   size_t blocks = (bytes / 16 + 255) / 256;
   if (blocks < 1) blocks = 1;
   if (blocks > 1024) blocks = 1024;
-  k_zero<<<(unsigned)blocks, 256, 0, s>>>((uint8_t*)p, bytes);
-  return hipGetLastError();
+  return launch_kernel(MOE_KERNEL_ZERO, k_zero, dim3((unsigned)blocks), dim3(256), 0, s, (uint8_t*)p,
+                       bytes);
 }
 
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s) {
-  k_stream_read<<<4096, 256, 0, s>>>((const uint4*)src, bytes / 16, sink);
-  return hipGetLastError();
+  return launch_kernel(MOE_KERNEL_STREAM_READ, k_stream_read, dim3(4096), dim3(256), 0, s,
+                       (const uint4*)src, bytes / 16, sink);
+}
+
+hipError_t launch_delay(uint32_t microseconds, hipStream_t s) {
+  return launch_kernel(MOE_KERNEL_DELAY, k_delay, dim3(1), dim3(64), 0, s,
+                       (uint64_t)microseconds * 100u);
 }
 
 }  // namespace moe

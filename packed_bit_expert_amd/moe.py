@@ -38,7 +38,8 @@ EXPORTS = [
     "moe_w4a16_workspace_bytes", "moe_w4a16_workspace_init", "moe_w4a16_forward",
     "moe_w4a16_forward_debug", "moe_w4a16_stack_forward", "moe_w4a16_dequant",
     "moe_w4a16_combine", "moe_w4a16_sort_pairs", "moe_w4a16_device_status",
-    "moe_w4a16_stream_read",
+    "moe_w4a16_stream_read", "moe_w4a16_delay", "moe_w4a16_timing_begin",
+    "moe_w4a16_timing_end",
 ]
 
 
@@ -56,6 +57,11 @@ class Cfg(C.Structure):
         ("residual", C.c_void_p), ("prenorm_eps", C.c_float), ("reserved0", C.c_int32),
         ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t), ("stream", C.c_void_p),
     ]
+
+
+KERNEL_KINDS = {1: "decode gate/up", 2: "decode down + combine", 3: "slot resolve",
+                4: "batched gate/up GEMM", 5: "batched down GEMM", 6: "combine", 7: "sort",
+                8: "dequant", 9: "stream read", 10: "workspace fill", 11: "delay"}
 
 
 class Dump(C.Structure):
@@ -87,6 +93,9 @@ def lib():
             "moe_w4a16_sort_pairs": (C.c_int, [P, I32, I32, I32, P, P, P, P]),
             "moe_w4a16_device_status": (C.c_int, [P, C.POINTER(C.c_int32), P]),
             "moe_w4a16_stream_read": (C.c_int, [P, SZ, P, P]),
+            "moe_w4a16_delay": (C.c_int, [C.c_uint32, P]),
+            "moe_w4a16_timing_begin": (C.c_int, [I32]),
+            "moe_w4a16_timing_end": (C.c_int, [C.POINTER(C.c_float), C.POINTER(C.c_int32), I32]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -212,3 +221,21 @@ def moe_w4a16_device_status(workspace, stream=0) -> int:
 def moe_w4a16_stream_read(src, nbytes, sink, stream=0):
     _check(lib().moe_w4a16_stream_read(_p(src), nbytes, _p(sink),
                                        None if stream == 0 else _stream(stream)))
+
+
+def moe_w4a16_delay(microseconds: int, stream=0):
+    _check(lib().moe_w4a16_delay(microseconds, None if stream == 0 else _stream(stream)))
+
+
+def moe_w4a16_timing_begin(capacity: int):
+    _check(lib().moe_w4a16_timing_begin(capacity))
+
+
+def moe_w4a16_timing_end(capacity: int):
+    """Per-launch (milliseconds, MOE_KERNEL_* kind) lists, in launch order."""
+    ms = (C.c_float * capacity)()
+    kinds = (C.c_int32 * capacity)()
+    n = lib().moe_w4a16_timing_end(ms, kinds, capacity)
+    if n < 0:
+        _check(n)
+    return list(ms[:n]), list(kinds[:n])

@@ -131,3 +131,21 @@ def test_stack_and_hook_errors():
         M.moe_w4a16_stream_read(FAKE, 100, FAKE)
     assert ei.value.code == M.ERR_MISALIGNED
     assert "16-byte" in M.moe_w4a16_last_error()
+
+
+def test_measurement_helpers_reject_bad_arguments():
+    with pytest.raises(M.MoeError) as e:
+        M.moe_w4a16_delay(1_000_001)
+    assert e.value.code == M.ERR_INVALID_ARG
+    with pytest.raises(M.MoeError) as e:
+        M.moe_w4a16_timing_begin(0)
+    assert e.value.code == M.ERR_INVALID_ARG
+    with pytest.raises(M.MoeError) as e:
+        M.moe_w4a16_timing_end(16)  # never begun on this thread
+    assert e.value.code == M.ERR_INVALID_ARG
+
+
+def test_kernel_kind_constants_match_header():
+    src = open(os.path.join(ROOT, "include", "moe_w4a16.h")).read()
+    kinds = {int(v): n for n, v in re.findall(r"#define MOE_KERNEL_(\w+) (\d+)", src)}
+    assert sorted(kinds) == sorted(M.KERNEL_KINDS)
