@@ -33,7 +33,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=64)
     p.add_argument("--warmup", type=int, default=64)
-    p.add_argument("--workload", default="c1", choices=["c1", "c0", "c2", "c2stack", "c3", "c4", "c4b32"])
+    p.add_argument("--workload", default="c1",
+                   choices=["c1", "c0", "c2", "c2stack", "c3", "c4", "c4b32", "c1serial"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--calib", action="store_true",
@@ -68,9 +69,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     shape = S.LFM24B
-    wname = {"c2stack": "c2"}.get(args.workload, args.workload)
+    wname = {"c2stack": "c2", "c1serial": "c1"}.get(args.workload, args.workload)
     w = S.WORKLOADS[wname]
-    stack = args.workload in ("c1", "c2stack")
+    stack = args.workload in ("c1", "c2stack", "c1serial")
     T, E, K, H = w.tokens, shape.experts, shape.top_k, shape.hidden
     # layers resident: the whole 38-layer stack for every workload, so single-
     # layer workloads rotate over 38 layers and the reuse distance (762 MB+ per
@@ -99,7 +100,8 @@ def main():
     out = torch.empty((nsteps, T, H), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.Stream()  # capture needs a non-default stream; every launch and event uses it
     torch.cuda.set_stream(stream)
-    cfg = M.make_cfg(T, H, shape.inter, E, K, w.fmt, prenorm_eps=EPS, stream=stream)
+    cfg = M.make_cfg(T, H, shape.inter, E, K, w.fmt, prenorm_eps=EPS, stream=stream,
+                     flags=M.FLAG_SERIAL if args.workload == "c1serial" else 0)
     if w.fmt == S.FMT_E4M3_G16:
         cfg.tensor_scales = store.tscales[0].data_ptr()
     ws = torch.zeros(M.moe_w4a16_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
@@ -150,7 +152,10 @@ def main():
         distinct = [len(np.unique(ids_h[s])) for s in range(args.steps)]
     layer_calls = len(distinct)
     act = T * H * 2
-    per_kind = kernel_bytes(shape, w, T, float(np.mean(distinct)), chained=w.chained)
+    if args.workload == "c1serial":
+        per_kind = kernel_bytes_serial(shape, w, T)
+    else:
+        per_kind = kernel_bytes(shape, w, T, float(np.mean(distinct)), chained=w.chained)
     alg_bytes = sum(distinct) * shape.expert_bytes(w.fmt) + layer_calls * act * (3 if w.chained else 2)
     secs = ms / 1e3
     achieved_step = alg_bytes / secs / 1e9
@@ -281,6 +286,15 @@ def kernel_bytes(shape, w, T, distinct, chained):
             4: distinct * gu + act, 5: distinct * dn, 6: act * (2 if chained else 1)}
 
 
+def kernel_bytes_serial(shape, w, T):
+    """As kernel_bytes for serial expert execution: each gate/up and down
+    launch reads one expert; the combine reads the residual and writes out."""
+    H, I = shape.hidden, shape.inter
+    G = shape.group(w.fmt)
+    act = T * H * 2
+    return {1: 2 * I * (H // 2 + H // G) + act, 2: H * (I // 2 + I // G), 6: 2 * act}
+
+
 def kernel_flops(shape, T, kind):
     H, I, K = shape.hidden, shape.inter, shape.top_k
     return 2 * T * K * (2 * I * H if kind == 4 else H * I)
@@ -379,6 +393,8 @@ def pmc_summary(args):
 def workload_name(k):
     return {
         "c1": "38-layer MoE stack, batch-1 decode (LFM2.5-24B-A2B, 2048/1536, 64 experts, top-4, E2M1+E8M0/32)",
+        "c1serial": "38-layer MoE stack, batch-1 decode, serial expert execution (ablation: one "
+                    "gate/up and one down launch per selected expert, then the combine)",
         "c0": "one MoE layer, 1 token (rotating over 38 resident layers)",
         "c2": "concurrency-32 decode, Zipf(1.1) routing, one layer per call (rotating over 38 layers)",
         "c2stack": "concurrency-32 decode through the 38-layer stack",

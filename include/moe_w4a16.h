@@ -90,6 +90,13 @@ extern "C" {
 #define MOE_FLAG_FORCE_DECODE (1u << 1)   /* use the per-token GEMV path for any T */
 #define MOE_FLAG_FORCE_BATCHED (1u << 2)  /* use the sorted MFMA path even at T = 1 */
 #define MOE_FLAG_CHECK_IDS (1u << 3)      /* device-side id / alignment checks */
+/* Serial expert execution, the ablation of the grouped engine ("LFM2.5-24B-A2B
+ * -- Packed MXFP4 Inference", "Grouped top-4 expert execution": the original
+ * runner executed each selected expert separately).  T = 1 on the decode path
+ * only: every slot j runs its own gate/up and down launches, which write y_j,
+ * and one combine launch follows (2k + 1 launches per layer instead of 2).
+ * Same device functions, so the results equal the grouped path's bit for bit. */
+#define MOE_FLAG_SERIAL (1u << 4)
 
 typedef struct moe_w4a16_cfg {
   int32_t abi_version;         /* MOE_W4A16_ABI_VERSION */

@@ -61,7 +61,7 @@ bool capturing(hipStream_t s) {
 constexpr int kStackGroup = 64;  // layers whose routing slots are resolved in one pass
 
 struct Layout {
-  size_t hbuf, ybuf, ping, slots, total;
+  size_t hbuf, ybuf, ping, scratch, slots, total;
 };
 
 Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
@@ -72,6 +72,8 @@ Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
   L.ybuf = off;
   off += align256((size_t)(T * K * H) * 2);
   L.ping = off;
+  off += align256((size_t)(T * H) * 2);
+  L.scratch = off;  // serial mode: the per-slot launches' unused combine output
   off += align256((size_t)(T * H) * 2);
   L.slots = off;
   off += align256((size_t)(T * K) * kStackGroup * sizeof(SlotRef));
@@ -95,10 +97,14 @@ int check_shape(const moe_w4a16_cfg* c) {
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "hidden %d / inter %d not supported", c->hidden,
                 c->inter);
   const uint32_t known = MOE_FLAG_PRENORM | MOE_FLAG_FORCE_DECODE | MOE_FLAG_FORCE_BATCHED |
-                         MOE_FLAG_CHECK_IDS;
+                         MOE_FLAG_CHECK_IDS | MOE_FLAG_SERIAL;
   if (c->flags & ~known) return fail(MOE_ERR_INVALID_ARG, "unknown flag bits 0x%x", c->flags);
   if ((c->flags & MOE_FLAG_FORCE_DECODE) && (c->flags & MOE_FLAG_FORCE_BATCHED))
     return fail(MOE_ERR_INVALID_ARG, "FORCE_DECODE and FORCE_BATCHED together");
+  if ((c->flags & MOE_FLAG_SERIAL) &&
+      (c->num_tokens > 1 || (c->flags & MOE_FLAG_FORCE_BATCHED) ||
+       !decode_supported(c->hidden, c->inter)))
+    return fail(MOE_ERR_INVALID_ARG, "MOE_FLAG_SERIAL needs T <= 1 on the decode path");
   if ((c->flags & MOE_FLAG_FORCE_DECODE) && !decode_supported(c->hidden, c->inter))
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "no decode kernel for hidden %d / inter %d",
                 c->hidden, c->inter);
@@ -159,6 +165,36 @@ int check_call(const moe_w4a16_cfg* c, const Call& k) {
   return MOE_OK;
 }
 
+// Serial expert execution (T = 1): slot j as a one-slot decode layer whose
+// down launch writes y_j (its own one-slot combine goes to scratch), then the
+// slot-order combine of all y_j with the residual.
+int run_serial(const moe_w4a16_cfg* c, const DecodeArgs& a, uint16_t* ybuf, uint16_t* scratch,
+               hipStream_t s) {
+  const int K = a.K, H = a.H, I = a.I;
+  uint16_t* y = a.dy ? a.dy : ybuf;
+  for (int j = 0; j < K; ++j) {
+    DecodeArgs b = a;
+    b.ids = a.ids + j;
+    b.rw = a.rw + j;
+    b.K = 1;
+    b.hbuf = a.hbuf + (size_t)j * I;
+    b.slots = a.slots + j;
+    b.pre = a.pre ? a.pre + j : nullptr;
+    b.residual = nullptr;
+    b.out = scratch;
+    b.du = j == 0 ? a.du : nullptr;
+    b.dg = a.dg ? a.dg + (size_t)j * I : nullptr;
+    b.dv = a.dv ? a.dv + (size_t)j * I : nullptr;
+    b.dh = a.dh ? a.dh + (size_t)j * I : nullptr;
+    b.dy = y + (size_t)j * H;
+    const hipError_t e = launch_decode(b, c->scale_fmt, s);
+    if (e != hipSuccess) return hip_fail(e, "decode launch (serial slot)");
+  }
+  const hipError_t e = launch_combine(y, a.rw, a.residual, a.out, 1, K, H, s);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return ok();
+}
+
 int run_layer(const moe_w4a16_cfg* c, const Call& k, const SlotRef* pre = nullptr) {
   const int T = c->num_tokens;
   if (T == 0) return ok();
@@ -194,6 +230,8 @@ int run_layer(const moe_w4a16_cfg* c, const Call& k, const SlotRef* pre = nullpt
     a.E = c->num_experts;
     a.flags = c->flags;
     a.eps = c->prenorm_eps;
+    if (c->flags & MOE_FLAG_SERIAL) return run_serial(c, a, (uint16_t*)(ws + L.ybuf),
+                                                      (uint16_t*)(ws + L.scratch), s);
     e = launch_decode(a, c->scale_fmt, s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return ok();

@@ -149,3 +149,11 @@ def test_kernel_kind_constants_match_header():
     src = open(os.path.join(ROOT, "include", "moe_w4a16.h")).read()
     kinds = {int(v): n for n, v in re.findall(r"#define MOE_KERNEL_(\w+) (\d+)", src)}
     assert sorted(kinds) == sorted(M.KERNEL_KINDS)
+
+
+def test_serial_flag_limits():
+    for over in ({"T": 2}, {"flags": M.FLAG_SERIAL | M.FLAG_FORCE_BATCHED}):
+        c = cfg(**{"flags": M.FLAG_SERIAL, **over})
+        with pytest.raises(M.MoeError) as e:
+            call(c)
+        assert e.value.code == M.ERR_INVALID_ARG

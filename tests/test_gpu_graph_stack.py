@@ -135,9 +135,9 @@ def _chain_single(store, x, ids, rw, T, eps=GH.EPS):
     return [GH.bits_host(o) for o in outs]
 
 
-def _stack(store, x, ids, rw, T, L):
+def _stack(store, x, ids, rw, T, L, flags=0):
     out = torch.empty((T, LFM.hidden), dtype=torch.bfloat16, device=GH.dev())
-    cfg = M.make_cfg(T, prenorm_eps=GH.EPS)
+    cfg = M.make_cfg(T, flags=flags, prenorm_eps=GH.EPS)
     ws = torch.zeros(M.moe_w4a16_workspace_bytes(cfg), dtype=torch.uint8, device=GH.dev())
     cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), ws.numel()
     M.moe_w4a16_stack_forward(L, GH.bf16_dev(x), GH.i32_dev(ids), GH.bf16_dev(rw), store.wtab,
@@ -176,6 +176,8 @@ def test_c1_stack_full_size(stack_store):
         got = _stack(stack_store, x, ids, rw, 1, L)
         chain = _chain_single(stack_store, x, ids, rw, 1)
         assert np.array_equal(got, chain[-1]), "stack call == 38 single-layer calls"
+        serial = _stack(stack_store, x, ids, rw, 1, L, flags=M.FLAG_SERIAL)
+        assert np.array_equal(got, serial), "serial expert execution == grouped"
         ref = _teacher_forced(stack_store, x, ids, rw, L, f"c1 step{step}")
         GH.compare(got, ref, "c1 free-running 38-layer drift", check=False)
 

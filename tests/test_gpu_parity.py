@@ -298,3 +298,36 @@ def test_check_ids_flags_bad_slots(layer_mx):
     # a valid call afterwards reports 0
     _, st3 = layer_mx.gpu(x, ids, rw, flags=M.FLAG_CHECK_IDS)
     assert st3 == 0
+
+
+@pytest.mark.parametrize("fmt_layer,prenorm", [("layer_mx", False), ("layer_mx", True), ("layer_nv", False)])
+def test_serial_expert_execution_equals_grouped(fmt_layer, prenorm, request):
+    """The serial ablation (one gate/up and one down launch per selected
+    expert, then the combine) runs the same device functions as the grouped
+    path, so every dump and the output are bitwise equal to it; both are
+    checked against the oracle."""
+    L = request.getfixturevalue(fmt_layer)
+    banner(f"serial expert execution vs grouped ({fmt_layer}, prenorm={prenorm})")
+    w = S.WORKLOADS["c4" if L.fmt else "c0"]
+    for step in (0, 9):
+        x, ids, rw = S.inputs(w, 0, step)
+        res = x if prenorm else None
+        fl = M.FLAG_PRENORM if prenorm else 0
+        g_out, g_d, g_st = L.gpu(x, ids, rw, residual=res, flags=fl, dumps=True)
+        s_out, s_d, s_st = L.gpu(x, ids, rw, residual=res, flags=fl | M.FLAG_SERIAL, dumps=True)
+        assert g_st == s_st == 0
+        for k in ("u", "g", "v", "h", "y"):
+            assert np.array_equal(g_d[k], s_d[k]), k
+        assert np.array_equal(g_out, s_out)
+        GH.compare(s_out, L.oracle(x, ids, rw, residual=res, prenorm=prenorm), "out")
+
+
+def test_serial_check_ids(layer_mx):
+    banner("serial expert execution with a rejected slot")
+    x, ids, rw = S.inputs(S.WORKLOADS["c0"], 0, 5)
+    bad = ids.copy()
+    bad[0, 1] = 99
+    g_out, g_st = layer_mx.gpu(x, bad, rw, flags=M.FLAG_CHECK_IDS)
+    s_out, s_st = layer_mx.gpu(x, bad, rw, flags=M.FLAG_CHECK_IDS | M.FLAG_SERIAL)
+    assert g_st == s_st == 1
+    assert np.array_equal(g_out, s_out)
