@@ -339,6 +339,60 @@ int oracle_moe_forward(int T, int H, int I, int E, int K, int fmt,
     return 0;
 }
 
+/* ---------------------------------------------------------------------- */
+/* Router                                                                  */
+/* ---------------------------------------------------------------------- */
+
+/* The router of a fully GPU-resident layer ([MXFP4 card], "GPU routing
+ * inside resident-layer graphs"): router projection, sigmoid scores, expert
+ * bias where configured, dynamic top-k selection, routing coefficients.
+ * Readings where the card is silent:
+ *   u         = x[t], or the weightless RMS pre-norm of x[t] (as the layer)
+ *   logit[e]  = sum_k u[k] * Wr[e][k]     (BF16 router rows [E][H], fp64, k ascending)
+ *   s[e]      = 1 / (1 + exp(-logit[e]))
+ *   c[e]      = s[e] + bias[e]             (bias FP32 [E]; 0 when not configured)
+ *   slots     = the k experts of largest c, in descending c; equal c -> smaller e
+ *   w[t][j]   = bf16( s[e_j] / sum_j' s[e_j'] )   (coefficients from the scores,
+ *               normalised over the selected experts; the bias only selects)
+ * logits_out (optional) receives logit[t][e]. */
+int oracle_route(int T, int H, int E, int K, const uint16_t* x, const uint16_t* wr,
+                 const float* bias, int prenorm, double eps, int32_t* ids, uint16_t* rw,
+                 double* logits_out)
+{
+    if (K < 1 || K > E) return -1;
+    uint16_t* u = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
+    double* s = (double*)malloc(sizeof(double) * (size_t)E);
+    double* c = (double*)malloc(sizeof(double) * (size_t)E);
+    unsigned char* taken = (unsigned char*)malloc((size_t)E);
+    for (int t = 0; t < T; ++t) {
+        const uint16_t* xt = x + (size_t)t * H;
+        if (prenorm) oracle_prenorm(xt, u, H, eps);
+        else memcpy(u, xt, sizeof(uint16_t) * (size_t)H);
+        for (int e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int k = 0; k < H; ++k)
+                acc += oracle_f64_from_bf16(u[k]) * oracle_f64_from_bf16(wr[(size_t)e * H + k]);
+            if (logits_out) logits_out[(size_t)t * E + e] = acc;
+            s[e] = 1.0 / (1.0 + exp(-acc));
+            c[e] = s[e] + (bias ? (double)bias[e] : 0.0);
+            taken[e] = 0;
+        }
+        double sum = 0.0;
+        for (int j = 0; j < K; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e)
+                if (!taken[e] && (best < 0 || c[e] > c[best])) best = e;
+            taken[best] = 1;
+            ids[(size_t)t * K + j] = best;
+            sum += s[best];
+        }
+        for (int j = 0; j < K; ++j)
+            rw[(size_t)t * K + j] = oracle_bf16_from_f64(s[ids[(size_t)t * K + j]] / sum);
+    }
+    free(u); free(s); free(c); free(taken);
+    return 0;
+}
+
 int oracle_threads_available(void)
 {
 #ifdef _OPENMP

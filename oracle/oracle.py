@@ -62,6 +62,9 @@ def _declare(L):
         P, P, P, P, P, P, P, C.c_int, C.c_double, P, P, P, P, P, P, C.c_int]
     L.oracle_threads_available.restype = C.c_int
     L.oracle_threads_available.argtypes = []
+    L.oracle_route.restype = C.c_int
+    L.oracle_route.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P, P, P, C.c_int, C.c_double,
+                               P, P, P]
 
 
 def _ptr(a):
@@ -122,9 +125,13 @@ def combine(y, route_w, residual=None) -> np.ndarray:
 
 
 def prenorm(x, eps: float) -> np.ndarray:
+    """Weightless RMS pre-norm of every row of x (BF16 bits [..., H])."""
     x = _c(x, np.uint16)
     out = np.empty_like(x)
-    lib().oracle_prenorm(_ptr(x), _ptr(out), x.shape[-1], float(eps))
+    H = x.shape[-1]
+    xr, orr = x.reshape(-1, H), out.reshape(-1, H)
+    for r in range(xr.shape[0]):
+        lib().oracle_prenorm(_ptr(xr[r]), _ptr(orr[r]), H, float(eps))
     return out
 
 
@@ -195,3 +202,23 @@ def moe_forward(x, ids, route_w, nibbles, scales, *, hidden, inter, num_experts,
     if rc != 0:
         raise ValueError(f"oracle_moe_forward rejected the arguments (rc={rc})")
     return (out, d) if dumps else out
+
+
+def route(x, router_w, bias=None, *, top_k, prenorm=False, eps=1e-5, logits=False):
+    """Router of one layer (see oracle_route): x BF16 bits [T][H], router_w
+    BF16 bits [E][H], bias float32 [E] or None.  Returns ids int32 [T][k] and
+    route_w BF16 bits [T][k] (and the fp64 logits [T][E] if asked)."""
+    x = np.ascontiguousarray(x, np.uint16)
+    router_w = np.ascontiguousarray(router_w, np.uint16)
+    T, H = x.shape
+    E = router_w.shape[0]
+    assert router_w.shape == (E, H)
+    b = None if bias is None else np.ascontiguousarray(bias, np.float32)
+    ids = np.zeros((T, top_k), np.int32)
+    rw = np.zeros((T, top_k), np.uint16)
+    lg = np.zeros((T, E), np.float64)
+    rc = lib().oracle_route(T, H, E, top_k, _ptr(x), _ptr(router_w), _ptr(b), int(prenorm),
+                            float(eps), _ptr(ids), _ptr(rw), _ptr(lg))
+    if rc != 0:
+        raise ValueError(f"oracle_route: bad arguments (k={top_k}, E={E})")
+    return (ids, rw, lg) if logits else (ids, rw)

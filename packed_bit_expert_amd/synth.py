@@ -36,7 +36,7 @@ FMT_E8M0_G32 = 0
 FMT_E4M3_G16 = 1
 
 _ROOT = 2026
-S_NIB, S_SCALE, S_TSCALE, S_X, S_IDS, S_ROUTE_W, S_PERM = range(7)
+S_NIB, S_SCALE, S_TSCALE, S_X, S_IDS, S_ROUTE_W, S_PERM, S_ROUTER, S_BIAS = range(9)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -92,6 +92,20 @@ def expert_triplet(shape: Shape, fmt: int, layer: int, expert: int) -> np.ndarra
     """One expert as a contiguous byte buffer: nibbles, then scales."""
     return np.concatenate([expert_nibbles(shape, fmt, layer, expert),
                            expert_scales(shape, fmt, layer, expert)])
+
+
+def router_weights(shape: Shape, family: int, layer: int) -> np.ndarray:
+    """BF16 bits [E][H] of one layer's router projection: N(0, 1/H), so that a
+    unit-RMS input gives logits of unit variance."""
+    rng = _rng(family, S_ROUTER, layer, 0)
+    w = rng.standard_normal((shape.experts, shape.hidden), dtype=np.float32)
+    return to_bf16_bits(w / np.float32(np.sqrt(shape.hidden)))
+
+
+def expert_bias(shape: Shape, family: int, layer: int) -> np.ndarray:
+    """float32 [E] selection bias of one layer, uniform on [-0.05, 0.05]."""
+    rng = _rng(family, S_BIAS, layer, 0)
+    return rng.uniform(-0.05, 0.05, shape.experts).astype(np.float32)
 
 
 def tensor_scales(shape: Shape, fmt: int, layer: int) -> np.ndarray | None:
