@@ -34,7 +34,8 @@ def parse():
     p.add_argument("--steps", type=int, default=64)
     p.add_argument("--warmup", type=int, default=64)
     p.add_argument("--workload", default="c1",
-                   choices=["c1", "c0", "c2", "c2stack", "c3", "c4", "c4b32", "c1serial"])
+                   choices=["c1", "c0", "c2", "c2stack", "c3", "c4", "c4b32", "c1serial",
+                            "c1routed"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--calib", action="store_true",
@@ -69,9 +70,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     shape = S.LFM24B
-    wname = {"c2stack": "c2", "c1serial": "c1"}.get(args.workload, args.workload)
+    wname = {"c2stack": "c2", "c1serial": "c1", "c1routed": "c1"}.get(args.workload, args.workload)
+    routed = args.workload == "c1routed"
     w = S.WORKLOADS[wname]
-    stack = args.workload in ("c1", "c2stack", "c1serial")
+    stack = args.workload in ("c1", "c2stack", "c1serial", "c1routed")
     T, E, K, H = w.tokens, shape.experts, shape.top_k, shape.hidden
     # layers resident: the whole 38-layer stack for every workload, so single-
     # layer workloads rotate over 38 layers and the reuse distance (762 MB+ per
@@ -98,6 +100,14 @@ def main():
         ids = torch.from_numpy(np.stack([r[0] for r in routes])).to(dev)
         rws = torch.from_numpy(np.stack([r[1].view(np.int16) for r in routes])).view(torch.bfloat16).to(dev)
     out = torch.empty((nsteps, T, H), dtype=torch.bfloat16, device=dev)
+    if routed:
+        # the routing is an output of every step (router on the device)
+        ids = torch.zeros((nsteps, L, T, K), dtype=torch.int32, device=dev)
+        rws = torch.zeros((nsteps, L, T, K), dtype=torch.bfloat16, device=dev)
+        wr = torch.from_numpy(np.stack([S.router_weights(shape, w.family, l).view(np.int16)
+                                        for l in range(L)])).view(torch.bfloat16).to(dev)
+        rbias = torch.from_numpy(np.stack([S.expert_bias(shape, w.family, l)
+                                           for l in range(L)])).to(dev)
     stream = torch.cuda.Stream()  # capture needs a non-default stream; every launch and event uses it
     torch.cuda.set_stream(stream)
     cfg = M.make_cfg(T, H, shape.inter, E, K, w.fmt, prenorm_eps=EPS, stream=stream,
@@ -108,7 +118,10 @@ def main():
     cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), ws.numel()
 
     def step(s):
-        if stack:
+        if routed:
+            M.moe_w4a16_stack_forward_routed(L, xs[s], wr, rbias, store.wtab, store.stab, None,
+                                             out[s], ids[s], rws[s], cfg)
+        elif stack:
             ts = None if store.tscales is None else store.tscales
             M.moe_w4a16_stack_forward(L, xs[s], ids[s], rws[s], store.wtab, store.stab, ts,
                                       out[s], cfg)
@@ -283,7 +296,8 @@ def kernel_bytes(shape, w, T, distinct, chained):
     dn = H * (I // 2 + I // G)
     act = T * H * 2
     return {1: distinct * gu + act, 2: distinct * dn + act * (2 if chained else 1),
-            4: distinct * gu + act, 5: distinct * dn, 6: act * (2 if chained else 1)}
+            4: distinct * gu + act, 5: distinct * dn, 6: act * (2 if chained else 1),
+            12: shape.experts * H * 2 + act}
 
 
 def kernel_bytes_serial(shape, w, T):
@@ -395,6 +409,8 @@ def workload_name(k):
         "c1": "38-layer MoE stack, batch-1 decode (LFM2.5-24B-A2B, 2048/1536, 64 experts, top-4, E2M1+E8M0/32)",
         "c1serial": "38-layer MoE stack, batch-1 decode, serial expert execution (ablation: one "
                     "gate/up and one down launch per selected expert, then the combine)",
+        "c1routed": "38-layer MoE stack, batch-1 decode, routing on the device per layer (router "
+                    "projection, sigmoid, expert bias, top-4, coefficients) from the layer input",
         "c0": "one MoE layer, 1 token (rotating over 38 resident layers)",
         "c2": "concurrency-32 decode, Zipf(1.1) routing, one layer per call (rotating over 38 layers)",
         "c2stack": "concurrency-32 decode through the 38-layer stack",

@@ -193,6 +193,46 @@ int moe_w4a16_stack_forward(int32_t num_layers, const void* x, const int32_t* ex
                             const moe_w4a16_cfg* cfg);
 
 /*
+ * The layer's router on the device ("LFM2.5-24B-A2B -- Packed MXFP4
+ * Inference", "GPU routing inside resident-layer graphs": router projection,
+ * sigmoid scores, expert bias where configured, dynamic top-k, routing
+ * coefficients; nothing returns to the host):
+ *   u        = x[t], or its weightless RMS pre-norm with MOE_FLAG_PRENORM
+ *   logit[e] = sum_k u[k] * router_w[e][k]      (FP64)
+ *   s[e] = sigmoid(logit[e]);  key c[e] = s[e] + expert_bias[e]
+ *   expert_ids[t][0..k-1] = the k largest keys, descending; equal keys to
+ *                           the smaller id
+ *   route_w[t][j] = bf16(s[ids[t][j]] / sum over the k selected s)
+ *   x           device BF16 [T][H], 16-byte aligned
+ *   router_w    device BF16 [E][H], 16-byte aligned
+ *   expert_bias device FP32 [E], or NULL (no bias)
+ *   expert_ids  device int32 [T][k] (written);  route_w device BF16 [T][k] (written)
+ * Uses cfg->num_tokens, hidden, num_experts (<= 256), top_k, flags, prenorm_eps,
+ * workspace (the moe_w4a16_workspace_bytes of the cfg) and stream.
+ */
+int moe_w4a16_route(const void* x, const void* router_w, const float* expert_bias,
+                    int32_t* expert_ids, void* route_w, const moe_w4a16_cfg* cfg);
+
+/* moe_w4a16_route, then moe_w4a16_forward with the ids and coefficients it
+ * wrote (both stay on the device; the buffers are the caller's). */
+int moe_w4a16_forward_routed(const void* x, const void* router_w, const float* expert_bias,
+                             const void* const* packed_weights, const void* const* scales,
+                             void* out, int32_t* expert_ids, void* route_w,
+                             const moe_w4a16_cfg* cfg);
+
+/* moe_w4a16_stack_forward with the routing of every layer computed on the
+ * device from that layer's pre-normed input: layer l routes with
+ * router_w + l*E*H (BF16 [L][E][H]) and expert_bias + l*E (FP32 [L][E], or
+ * NULL), writing expert_ids + l*T*k and route_w + l*T*k ([L][T][k]), then
+ * runs its experts.  Each layer's routing depends on the previous layer's
+ * output, as in the model. */
+int moe_w4a16_stack_forward_routed(int32_t num_layers, const void* x, const void* router_w,
+                                   const float* expert_bias, const void* const* packed_weights,
+                                   const void* const* scales, const float* tensor_scales,
+                                   void* out, int32_t* expert_ids, void* route_w,
+                                   const moe_w4a16_cfg* cfg);
+
+/*
  * Test hook: dequantise one packed [rows][cols] matrix to BF16 with the same
  * device decoders the GEMM kernels use.  E2M1 * E8M0 and E2M1 * E4M3FN are
  * exact in BF16, so the result is the exact dequantised value ("Model and
@@ -257,6 +297,7 @@ int moe_w4a16_delay(uint32_t microseconds, void* stream);
 #define MOE_KERNEL_STREAM_READ 9     /* moe_w4a16_stream_read */
 #define MOE_KERNEL_ZERO 10           /* workspace fill */
 #define MOE_KERNEL_DELAY 11          /* moe_w4a16_delay */
+#define MOE_KERNEL_ROUTER 12         /* router projection, sigmoid, bias, top-k, coefficients */
 
 /*
  * Kernel timing (measurement only).  After moe_w4a16_timing_begin(capacity)

@@ -61,7 +61,7 @@ bool capturing(hipStream_t s) {
 constexpr int kStackGroup = 64;  // layers whose routing slots are resolved in one pass
 
 struct Layout {
-  size_t hbuf, ybuf, ping, scratch, slots, total;
+  size_t hbuf, ybuf, ping, scratch, logits, rcount, slots, total;
 };
 
 Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
@@ -75,6 +75,10 @@ Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
   off += align256((size_t)(T * H) * 2);
   L.scratch = off;  // serial mode: the per-slot launches' unused combine output
   off += align256((size_t)(T * H) * 2);
+  L.logits = off;  // router logits, FP64 [T][E]
+  off += align256((size_t)(T * E) * 8);
+  L.rcount = off;  // router: waves done per token (zero between calls)
+  off += align256((size_t)T * 4);
   L.slots = off;
   off += align256((size_t)(T * K) * kStackGroup * sizeof(SlotRef));
   L.total = off;
@@ -434,6 +438,109 @@ int moe_w4a16_stream_read(const void* src, size_t bytes, void* sink, void* strea
 }
 
 }  // extern "C"
+
+namespace {
+
+int check_route(const moe_w4a16_cfg* c, const void* x, const void* router_w,
+                const float* expert_bias, const int32_t* ids, const void* rw) {
+  int rc = check_shape(c);
+  if (rc) return rc;
+  if (!router_supported(c->hidden, c->num_experts, c->top_k))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE,
+                "router needs hidden 512, 1024, 1536 or 2048, num_experts <= 256, top_k <= num_experts");
+  if (c->num_tokens == 0) return MOE_OK;
+  if (!x || !router_w || !ids || !rw) return fail(MOE_ERR_INVALID_ARG, "NULL router argument");
+  if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(ids, 4) || !aligned(rw, 2) ||
+      (expert_bias && !aligned(expert_bias, 4)))
+    return fail(MOE_ERR_MISALIGNED, "router arguments misaligned (x, router_w: 16 bytes)");
+  if (!c->workspace) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(c->workspace, 256)) return fail(MOE_ERR_MISALIGNED, "workspace not 256-byte aligned");
+  const size_t need = moe_w4a16_workspace_bytes(c);
+  if (c->workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", c->workspace_bytes,
+                need);
+  return MOE_OK;
+}
+
+int run_route(const moe_w4a16_cfg* c, const void* x, const void* router_w, const float* bias,
+              int32_t* ids, void* rw) {
+  const int T = c->num_tokens;
+  if (T == 0) return ok();
+  const Layout L = layout(T, c->hidden, c->inter, c->num_experts, c->top_k);
+  const hipError_t e = launch_route(
+      (const uint16_t*)x, (const uint16_t*)router_w, bias, T, c->hidden, c->num_experts, c->top_k,
+      (c->flags & MOE_FLAG_PRENORM) != 0, c->prenorm_eps,
+      (double*)((uint8_t*)c->workspace + L.logits), (uint32_t*)((uint8_t*)c->workspace + L.rcount),
+      ids, (uint16_t*)rw, (hipStream_t)c->stream);
+  if (e != hipSuccess) return hip_fail(e, "router launch");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" int moe_w4a16_route(const void* x, const void* router_w, const float* expert_bias,
+                               int32_t* expert_ids, void* route_w, const moe_w4a16_cfg* cfg) {
+  const int rc = check_route(cfg, x, router_w, expert_bias, expert_ids, route_w);
+  if (rc) return rc;
+  return run_route(cfg, x, router_w, expert_bias, expert_ids, route_w);
+}
+
+extern "C" int moe_w4a16_forward_routed(const void* x, const void* router_w,
+                                        const float* expert_bias,
+                                        const void* const* packed_weights,
+                                        const void* const* scales, void* out, int32_t* expert_ids,
+                                        void* route_w, const moe_w4a16_cfg* cfg) {
+  int rc = check_route(cfg, x, router_w, expert_bias, expert_ids, route_w);
+  if (rc) return rc;
+  Call k{x, expert_ids, route_w, packed_weights, scales, cfg->tensor_scales, cfg->residual, out,
+         nullptr};
+  rc = check_call(cfg, k);
+  if (rc) return rc;
+  rc = run_route(cfg, x, router_w, expert_bias, expert_ids, route_w);
+  if (rc) return rc;
+  return run_layer(cfg, k);
+}
+
+extern "C" int moe_w4a16_stack_forward_routed(int32_t num_layers, const void* x,
+                                              const void* router_w, const float* expert_bias,
+                                              const void* const* packed_weights,
+                                              const void* const* scales,
+                                              const float* tensor_scales, void* out,
+                                              int32_t* expert_ids, void* route_w,
+                                              const moe_w4a16_cfg* cfg) {
+  if (num_layers < 1) return fail(MOE_ERR_INVALID_ARG, "num_layers %d < 1", num_layers);
+  if (!cfg) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+  moe_w4a16_cfg lc = *cfg;
+  lc.flags |= MOE_FLAG_PRENORM;
+  lc.tensor_scales = tensor_scales;
+  lc.residual = x;
+  int rc = check_route(&lc, x, router_w, expert_bias, expert_ids, route_w);
+  if (rc) return rc;
+  Call k{x, expert_ids, route_w, packed_weights, scales, tensor_scales, x, out, nullptr};
+  rc = check_call(&lc, k);
+  if (rc) return rc;
+  const int64_t T = lc.num_tokens, K = lc.top_k, E = lc.num_experts, H = lc.hidden;
+  if (T == 0) return ok();
+  const Layout L = layout(T, lc.hidden, lc.inter, E, K);
+  void* ping = (uint8_t*)lc.workspace + L.ping;
+  const void* src = x;
+  for (int l = 0; l < num_layers; ++l) {
+    void* dst = ((num_layers - 1 - l) % 2 == 0) ? out : ping;
+    int32_t* ids_l = expert_ids + (size_t)l * T * K;
+    void* rw_l = (uint16_t*)route_w + (size_t)l * T * K;
+    rc = run_route(&lc, src, (const uint16_t*)router_w + (size_t)l * E * H,
+                   expert_bias ? expert_bias + (size_t)l * E : nullptr, ids_l, rw_l);
+    if (rc) return rc;
+    lc.residual = src;
+    lc.tensor_scales = tensor_scales ? tensor_scales + (size_t)l * E * 2 : nullptr;
+    Call kl{src, ids_l, rw_l, packed_weights + (size_t)l * E, scales + (size_t)l * E,
+            lc.tensor_scales, src, dst, nullptr};
+    rc = run_layer(&lc, kl);
+    if (rc) return rc;
+    src = dst;
+  }
+  return ok();
+}
 
 namespace moe {
 

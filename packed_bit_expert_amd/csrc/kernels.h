@@ -78,6 +78,12 @@ hipError_t launch_dequant(const uint8_t* nib, const uint8_t* sc, int rows, int c
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_delay(uint32_t microseconds, hipStream_t s);
+bool router_supported(int H, int E, int K);
+// logits [T][E] FP64 and count [T] (zero, left zero) workspace; ids [T][K];
+// rw [T][K] BF16
+hipError_t launch_route(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H,
+                        int E, int K, bool prenorm, float eps, double* logits, uint32_t* count,
+                        int32_t* ids, uint16_t* rw, hipStream_t s);
 
 // Kernel timing (moe_w4a16_timing_*): while the calling thread times
 // launches, each launch gets a start and a stop event that the dispatch

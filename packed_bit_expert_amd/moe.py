@@ -40,7 +40,8 @@ EXPORTS = [
     "moe_w4a16_forward_debug", "moe_w4a16_stack_forward", "moe_w4a16_dequant",
     "moe_w4a16_combine", "moe_w4a16_sort_pairs", "moe_w4a16_device_status",
     "moe_w4a16_stream_read", "moe_w4a16_delay", "moe_w4a16_timing_begin",
-    "moe_w4a16_timing_end",
+    "moe_w4a16_timing_end", "moe_w4a16_route", "moe_w4a16_forward_routed",
+    "moe_w4a16_stack_forward_routed",
 ]
 
 
@@ -62,7 +63,8 @@ class Cfg(C.Structure):
 
 KERNEL_KINDS = {1: "decode gate/up", 2: "decode down + combine", 3: "slot resolve",
                 4: "batched gate/up GEMM", 5: "batched down GEMM", 6: "combine", 7: "sort",
-                8: "dequant", 9: "stream read", 10: "workspace fill", 11: "delay"}
+                8: "dequant", 9: "stream read", 10: "workspace fill", 11: "delay",
+                12: "router"}
 
 
 class Dump(C.Structure):
@@ -95,6 +97,10 @@ def lib():
             "moe_w4a16_device_status": (C.c_int, [P, C.POINTER(C.c_int32), P]),
             "moe_w4a16_stream_read": (C.c_int, [P, SZ, P, P]),
             "moe_w4a16_delay": (C.c_int, [C.c_uint32, P]),
+            "moe_w4a16_route": (C.c_int, [P, P, P, P, P, C.POINTER(Cfg)]),
+            "moe_w4a16_forward_routed": (C.c_int, [P, P, P, P, P, P, P, P, C.POINTER(Cfg)]),
+            "moe_w4a16_stack_forward_routed": (C.c_int, [I32, P, P, P, P, P, P, P, P, P,
+                                                         C.POINTER(Cfg)]),
             "moe_w4a16_timing_begin": (C.c_int, [I32]),
             "moe_w4a16_timing_end": (C.c_int, [C.POINTER(C.c_float), C.POINTER(C.c_int32), I32]),
         }
@@ -240,3 +246,23 @@ def moe_w4a16_timing_end(capacity: int):
     if n < 0:
         _check(n)
     return list(ms[:n]), list(kinds[:n])
+
+
+def moe_w4a16_route(x, router_w, expert_bias, expert_ids, route_w, cfg: Cfg):
+    _check(lib().moe_w4a16_route(_p(x), _p(router_w), _p(expert_bias), _p(expert_ids),
+                                 _p(route_w), C.byref(cfg)))
+
+
+def moe_w4a16_forward_routed(x, router_w, expert_bias, packed_weights, scales, out, expert_ids,
+                             route_w, cfg: Cfg):
+    _check(lib().moe_w4a16_forward_routed(_p(x), _p(router_w), _p(expert_bias),
+                                          _p(packed_weights), _p(scales), _p(out),
+                                          _p(expert_ids), _p(route_w), C.byref(cfg)))
+
+
+def moe_w4a16_stack_forward_routed(num_layers, x, router_w, expert_bias, packed_weights, scales,
+                                   tensor_scales, out, expert_ids, route_w, cfg: Cfg):
+    _check(lib().moe_w4a16_stack_forward_routed(num_layers, _p(x), _p(router_w),
+                                                _p(expert_bias), _p(packed_weights), _p(scales),
+                                                _p(tensor_scales), _p(out), _p(expert_ids),
+                                                _p(route_w), C.byref(cfg)))

@@ -157,3 +157,18 @@ def test_serial_flag_limits():
         with pytest.raises(M.MoeError) as e:
             call(c)
         assert e.value.code == M.ERR_INVALID_ARG
+
+
+def test_router_zero_tokens_and_bad_shape():
+    cfg = M.make_cfg(0)
+    M.moe_w4a16_route(0, 0, None, 0, 0, cfg)
+    c2 = M.make_cfg(1, num_experts=300, top_k=4)
+    c2.workspace, c2.workspace_bytes = FAKE, 1 << 30
+    with pytest.raises(M.MoeError) as e:
+        M.moe_w4a16_route(FAKE, FAKE, None, FAKE, FAKE, c2)
+    assert e.value.code == M.ERR_UNSUPPORTED_SHAPE
+    c3 = M.make_cfg(1, top_k=4)
+    c3.workspace, c3.workspace_bytes = FAKE, 16
+    with pytest.raises(M.MoeError) as e:
+        M.moe_w4a16_route(FAKE, FAKE, None, FAKE, FAKE, c3)
+    assert e.value.code == M.ERR_WORKSPACE_TOO_SMALL

@@ -1,0 +1,222 @@
+"""GPU: the layer router on the device ("LFM2.5-24B-A2B -- Packed MXFP4
+Inference", "GPU routing inside resident-layer graphs"), against the oracle.
+
+The top-k choice is an integer decision taken from floating point.  Both
+sides compute the logits and scores in FP64 but not in the same order, so
+the ids must equal the oracle's wherever the oracle's keys are separated by
+more than FP64 rounding; where two keys are that close, either choice is
+valid and the test checks that the GPU's set is one of the valid ones.  The
+coefficients are compared under the layer tolerance and are expected to be
+bit-identical almost everywhere.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from packed_bit_expert_amd import moe as M
+from packed_bit_expert_amd import synth as S
+from packed_bit_expert_amd.residency import ResidentExperts
+from tests import gpu_helpers as GH
+
+pytestmark = pytest.mark.gpu
+LFM = S.LFM24B
+FAMILY = 1  # router weights of the c1 family
+TIE = 1e-12  # keys closer than this (relative) may legitimately order either way
+
+
+def banner(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def check_ids(gpu_ids, ref_ids, logits, bias, K):
+    """Exact where the oracle's keys are separated; valid where they tie."""
+    T = ref_ids.shape[0]
+    s = 1.0 / (1.0 + np.exp(-logits))
+    key = s if bias is None else s + bias.astype(np.float64)[None, :]
+    exact = 0
+    for t in range(T):
+        if np.array_equal(gpu_ids[t], ref_ids[t]):
+            exact += 1
+            continue
+        # every GPU pick must have a key within TIE of the oracle's key in that slot
+        kr = key[t, ref_ids[t]]
+        kg = key[t, gpu_ids[t]]
+        assert len(set(gpu_ids[t].tolist())) == K, f"token {t}: repeated ids {gpu_ids[t]}"
+        assert np.all(np.abs(kg - kr) <= TIE * np.abs(kr)), (
+            f"token {t}: ids {gpu_ids[t]} vs oracle {ref_ids[t]}, keys {kg} vs {kr}")
+    print(f"[parity] router ids: {exact}/{T} tokens identical, the rest within key ties", flush=True)
+
+
+def route_gpu(x, wr, bias, K, flags=0, E=None):
+    T, H = x.shape
+    E = wr.shape[0] if E is None else E
+    cfg = M.make_cfg(T, H, 1536 if H == 2048 else 256, E, K, flags=flags,
+                     prenorm_eps=GH.EPS)
+    ws = torch.zeros(max(M.moe_w4a16_workspace_bytes(cfg), 256), dtype=torch.uint8, device=GH.dev())
+    cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), ws.numel()
+    ids = torch.full((T, K), -1, dtype=torch.int32, device=GH.dev())
+    rw = torch.zeros((T, K), dtype=torch.bfloat16, device=GH.dev())
+    bd = None if bias is None else torch.from_numpy(bias).to(GH.dev())
+    M.moe_w4a16_route(GH.bf16_dev(x), GH.bf16_dev(wr), bd, ids, rw, cfg)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), GH.bits_host(rw)
+
+
+@pytest.mark.parametrize("T,bias,prenorm", [(1, False, True), (1, True, True), (32, True, False),
+                                            (64, False, False), (5, True, True)])
+def test_router_matches_oracle(T, bias, prenorm):
+    banner(f"router T={T} bias={bias} prenorm={prenorm}")
+    wr = S.router_weights(LFM, FAMILY, 0)
+    b = S.expert_bias(LFM, FAMILY, 0) if bias else None
+    x = S.activations(FAMILY, 0, 100 + T, T, LFM.hidden)
+    if prenorm:
+        x = S.to_bf16_bits(O.f64_from_bf16(x).astype(np.float32) * 19)
+    ids, rw = route_gpu(x, wr, b, 4, flags=M.FLAG_PRENORM if prenorm else 0)
+    rids, rrw, lg = O.route(x, wr, b, top_k=4, prenorm=prenorm, eps=GH.EPS, logits=True)
+    check_ids(ids, rids, lg, b, 4)
+    same = np.all(ids == rids, axis=1)
+    st = GH.compare(rw[same], rrw[same], "route_w")
+    assert st["bit_identical"] >= 0.99
+
+
+@pytest.mark.parametrize("E,K,H", [(8, 8, 512), (256, 8, 2048), (1, 1, 512), (64, 1, 2048),
+                                   (100, 6, 2048)])
+def test_router_edge_shapes(E, K, H):
+    banner(f"router edge E={E} K={K} H={H}")
+    rng = np.random.default_rng(E * 131 + K)
+    wr = S.to_bf16_bits(rng.standard_normal((E, H)).astype(np.float32) / np.float32(np.sqrt(H)))
+    b = rng.uniform(-0.05, 0.05, E).astype(np.float32)
+    x = S.to_bf16_bits(rng.standard_normal((7, H)).astype(np.float32))
+    ids, rw = route_gpu(x, wr, b, K)
+    rids, rrw, lg = O.route(x, wr, b, top_k=K, logits=True)
+    check_ids(ids, rids, lg, b, K)
+    same = np.all(ids == rids, axis=1)
+    GH.compare(rw[same], rrw[same], "route_w")
+
+
+def test_router_all_ties_closed_form():
+    """x orthogonal to every router row: all keys tie, the slots are experts
+    0..k-1 and every coefficient is bf16(1/k)."""
+    banner("router all-tie closed form")
+    H, E, K = 2048, 64, 4
+    rng = np.random.default_rng(9)
+    wr = S.to_bf16_bits(rng.standard_normal((E, H)).astype(np.float32))
+    wr[:, :8] = 0
+    x = np.zeros((3, H), np.uint16)
+    x[:, :8] = S.to_bf16_bits(rng.standard_normal((3, 8)).astype(np.float32))
+    ids, rw = route_gpu(x, wr, None, K)
+    assert ids.tolist() == [[0, 1, 2, 3]] * 3
+    assert np.all(rw == O.bf16_from_f64(0.25))
+
+
+@pytest.fixture(scope="module")
+def routed_stack():
+    banner("upload the 38-layer E8M0 stack and its routers")
+    st = ResidentExperts(LFM, S.FMT_E8M0_G32, LFM.layers).fill_synthetic()
+    wr = np.stack([S.router_weights(LFM, FAMILY, l) for l in range(LFM.layers)])
+    b = np.stack([S.expert_bias(LFM, FAMILY, l) for l in range(LFM.layers)])
+    yield st, wr, b, GH.bf16_dev(wr), torch.from_numpy(b).to(GH.dev())
+    del st
+    torch.cuda.empty_cache()
+
+
+def _routed_single(st, wrd, bd, x, L, T):
+    """The routed stack as L single-layer routed calls (pre-norm + residual)."""
+    h = GH.bf16_dev(x)
+    ids_all, outs = [], []
+    for l in range(L):
+        wt, stb, _ = st.layer_tables(l)
+        out = torch.empty_like(h)
+        ids = torch.empty((T, 4), dtype=torch.int32, device=GH.dev())
+        rw = torch.empty((T, 4), dtype=torch.bfloat16, device=GH.dev())
+        cfg = M.make_cfg(T, flags=M.FLAG_PRENORM, residual=h, prenorm_eps=GH.EPS)
+        ws = torch.zeros(M.moe_w4a16_workspace_bytes(cfg), dtype=torch.uint8, device=GH.dev())
+        cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), ws.numel()
+        M.moe_w4a16_forward_routed(h, wrd[l], bd[l], wt, stb, out, ids, rw, cfg)
+        ids_all.append(ids)
+        outs.append(out)
+        h = out
+    torch.cuda.synchronize()
+    return GH.bits_host(outs[-1]), np.stack([i.cpu().numpy() for i in ids_all])
+
+
+def _routed_stack(st, wrd, bd, x, L, T):
+    out = torch.empty((T, LFM.hidden), dtype=torch.bfloat16, device=GH.dev())
+    ids = torch.empty((L, T, 4), dtype=torch.int32, device=GH.dev())
+    rw = torch.empty((L, T, 4), dtype=torch.bfloat16, device=GH.dev())
+    cfg = M.make_cfg(T, prenorm_eps=GH.EPS)
+    ws = torch.zeros(M.moe_w4a16_workspace_bytes(cfg), dtype=torch.uint8, device=GH.dev())
+    cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), ws.numel()
+    M.moe_w4a16_stack_forward_routed(L, GH.bf16_dev(x), wrd, bd, st.wtab, st.stab, None, out, ids,
+                                     rw, cfg)
+    torch.cuda.synchronize()
+    return GH.bits_host(out), ids.cpu().numpy()
+
+
+@pytest.mark.parametrize("T", [1, 32])
+def test_routed_stack(routed_stack, T):
+    """38 layers whose routing is computed on the device from each layer's
+    input: the stack call equals 38 single-layer routed calls bit for bit,
+    and the first layers match the oracle (its own routing and layer) on the
+    oracle chain's input."""
+    st, wr, b, wrd, bd = routed_stack
+    L = LFM.layers
+    banner(f"routed 38-layer stack T={T}")
+    x = S.activations(FAMILY, 0, 7, T, LFM.hidden)
+    got, ids = _routed_stack(st, wrd, bd, x, L, T)
+    chain, ids_c = _routed_single(st, wrd, bd, x, L, T)
+    assert np.array_equal(got, chain) and np.array_equal(ids, ids_c)
+    h = x
+    for l in range(4 if T == 32 else 8):
+        lay = GH.Layer(LFM, S.FMT_E8M0_G32, l, store=st, l=l)
+        rids, rrw, lg = O.route(h, wr[l], b[l], top_k=4, prenorm=True, eps=GH.EPS, logits=True)
+        nxt = lay.oracle(h, rids, rrw, residual=h, prenorm=True)
+        # the GPU routes and runs layer l on the oracle chain's h_l
+        gl = torch.empty((T, LFM.hidden), dtype=torch.bfloat16, device=GH.dev())
+        gid = torch.empty((T, 4), dtype=torch.int32, device=GH.dev())
+        grw = torch.empty((T, 4), dtype=torch.bfloat16, device=GH.dev())
+        hd = GH.bf16_dev(h)
+        wt, stb, _ = st.layer_tables(l)
+        cfg = M.make_cfg(T, flags=M.FLAG_PRENORM, residual=hd, prenorm_eps=GH.EPS)
+        ws = torch.zeros(M.moe_w4a16_workspace_bytes(cfg), dtype=torch.uint8, device=GH.dev())
+        cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), ws.numel()
+        M.moe_w4a16_forward_routed(hd, wrd[l], bd[l], wt, stb, gl, gid, grw, cfg)
+        torch.cuda.synchronize()
+        check_ids(gid.cpu().numpy(), rids, lg, b[l], 4)
+        if np.array_equal(gid.cpu().numpy(), rids):
+            GH.compare(GH.bits_host(gl), nxt, f"routed layer {l}")
+        h = nxt
+
+
+def test_routed_stack_graph_replay(routed_stack):
+    """Captured once, replayed with new inputs: the routing is recomputed on
+    every replay and each replay equals the eager call."""
+    st, wr, b, wrd, bd = routed_stack
+    L, T = LFM.layers, 1
+    banner("routed stack under graph capture")
+    xin = torch.empty((T, LFM.hidden), dtype=torch.bfloat16, device=GH.dev())
+    out = torch.empty_like(xin)
+    ids = torch.empty((L, T, 4), dtype=torch.int32, device=GH.dev())
+    rw = torch.empty((L, T, 4), dtype=torch.bfloat16, device=GH.dev())
+    s = torch.cuda.Stream()
+    cfg = M.make_cfg(T, prenorm_eps=GH.EPS, stream=s)
+    ws = torch.zeros(M.moe_w4a16_workspace_bytes(cfg), dtype=torch.uint8, device=GH.dev())
+    cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), ws.numel()
+    xs = [S.activations(FAMILY, 0, 50 + r, T, LFM.hidden) for r in range(3)]
+    xin.copy_(GH.bf16_dev(xs[0]))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        M.moe_w4a16_stack_forward_routed(L, xin, wrd, bd, st.wtab, st.stab, None, out, ids, rw, cfg)
+    seen = []
+    for r in range(3):
+        xin.copy_(GH.bf16_dev(xs[r]))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref_out, ref_ids = _routed_stack(st, wrd, bd, xs[r], L, T)
+        assert np.array_equal(GH.bits_host(out), ref_out)
+        assert np.array_equal(ids.cpu().numpy(), ref_ids)
+        seen.append(ref_ids)
+    assert not np.array_equal(seen[0], seen[1])
