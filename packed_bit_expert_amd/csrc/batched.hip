@@ -106,7 +106,6 @@ __global__ __launch_bounds__(256) void k_sort(const int32_t* __restrict__ ids, i
 constexpr int kBW = 4;        // waves per workgroup
 constexpr int kBN = 16 * kBW; // output rows per workgroup
 constexpr int kMC = 16;       // tokens per LDS pass
-constexpr int kListCap = 2048;  // pair indices collected per scan pass
 
 template <int FMT, int NMAT>
 struct WStep {
@@ -114,19 +113,23 @@ struct WStep {
   uint32_t s[NMAT];
 };
 
+// K step ks of this lane's rows.  A rejected expert (ok = false) reads the
+// same 32 + 4 bytes of a harmless valid buffer for every step instead.
 template <int FMT, int NMAT>
 __device__ __forceinline__ void load_wstep(WStep<FMT, NMAT>& st, const uint8_t* const (&wrow)[2],
-                                           const uint8_t* const (&srow)[2], int ks, int g) {
+                                           const uint8_t* const (&srow)[2], int ks, int g,
+                                           bool ok) {
+  const int wo = ok ? ks * (kKS / 2) + 32 * g : 0;
 #pragma unroll
   for (int mt = 0; mt < NMAT; ++mt) {
     if constexpr (FMT == MOE_SCALE_E8M0_G32)
-      st.s[mt] = ldg<uint16_t>(srow[mt] + ks * (kKS / 32) + 2 * g);
+      st.s[mt] = ldg<uint16_t>(srow[mt] + (ok ? ks * (kKS / 32) + 2 * g : 0));
     else
-      st.s[mt] = ldg<uint32_t>(srow[mt] + ks * (kKS / 16) + 4 * g);
+      st.s[mt] = ldg<uint32_t>(srow[mt] + (ok ? ks * (kKS / 16) + 4 * g : 0));
   }
 #pragma unroll
   for (int mt = 0; mt < NMAT; ++mt) {
-    const uint8_t* src = wrow[mt] + ks * (kKS / 2) + 32 * g;
+    const uint8_t* src = wrow[mt] + wo;
     st.w[mt][0] = ldg16(src);
     st.w[mt][1] = ldg16(src + 16);
   }
@@ -166,30 +169,6 @@ __device__ __forceinline__ void wstep_mfma(const WStep<FMT, NMAT>& st, const uin
   }
 }
 
-// Stable scan of the routing ids for expert e: the pairs p = t*K + j with
-// ids[p] == e, in increasing p, whose rank lies in [r0, r0 + kListCap), go to
-// list[rank - r0].  Returns the expert's total pair count.  All threads of
-// the workgroup call it.
-__device__ int collect_pairs(const int32_t* ids, int npairs, int e, int r0, int* list,
-                             int* wcnt) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  int total = 0;
-  for (int base = 0; base < npairs; base += 64 * kBW) {
-    const int p = base + tid;
-    const bool m = p < npairs && ids[p] == e;
-    const uint64_t b = __ballot(m);
-    if (lane == 0) wcnt[wave] = __popcll(b);
-    __syncthreads();
-    int before = total;
-    for (int w = 0; w < wave; ++w) before += wcnt[w];
-    const int rank = before + __popcll(b & ((1ull << lane) - 1ull));
-    if (m && rank >= r0 && rank < r0 + kListCap) list[rank - r0] = p;
-    for (int w = 0; w < kBW; ++w) total += wcnt[w];
-    __syncthreads();
-  }
-  return total;
-}
-
 // Workgroup barrier for LDS data only.  __syncthreads() (and even an LDS-only
 // fence, because of the direct global->LDS loads) makes every wave wait for
 // all of its loads in flight, the weights included, at each barrier.  Here
@@ -201,6 +180,31 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4));  // lgkmcnt(0) only
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// Stable scan of the routing ids for expert e: the pairs p = t*K + j with
+// ids[p] == e, in increasing p, whose rank lies in [r0, r0 + kMC), go to
+// list[rank - r0].  All threads of the workgroup call it; id0 is the id of
+// pair tid (-1 past the end), read once when the workgroup starts, so calls
+// with at most 256 pairs touch no global memory.
+__device__ void collect_pairs(const int32_t* ids, int id0, int npairs, int e, int r0, int* list,
+                              int* wcnt) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int total = 0;
+  for (int base = 0; base < npairs; base += 64 * kBW) {
+    const int p = base + tid;
+    const int id = base == 0 ? id0 : (p < npairs ? ids[p] : -1);
+    const bool m = id == e;
+    const uint64_t b = __ballot(m);
+    if (lane == 0) wcnt[wave] = __popcll(b);
+    lds_barrier();
+    int before = total;
+    for (int w = 0; w < wave; ++w) before += wcnt[w];
+    const int rank = before + __popcll(b & ((1ull << lane) - 1ull));
+    if (m && rank >= r0 && rank < r0 + kMC) list[rank - r0] = p;
+    for (int w = 0; w < kBW; ++w) total += wcnt[w];
+    lds_barrier();
+  }
 }
 
 // s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maxima).
@@ -238,165 +242,276 @@ __device__ __forceinline__ void stage_rows(const BatchedArgs& a, const int* lp, 
   }
 }
 
-// One 16-token pass over staged A rows: optional RMS pre-norm (MODE 0), the
-// MFMAs over the whole contraction (blocks after the first are loaded here)
-// and the epilogue.  W holds the first block's steps on entry.
-template <int FMT, int MODE, int KB>
-__device__ __forceinline__ void gemm_pass(const BatchedArgs& a, WStep<FMT, (MODE == 0 ? 2 : 1)> (&W)[KB],
-                                          const uint8_t* const (&wrow)[2],
-                                          const uint8_t* const (&srow)[2], uint16_t* xs, int ldx,
-                                          const int* lp, int mcnt, int nkb, int n, int tile,
-                                          double tscale) {
+// The work of one call is a list of items -- (expert e, pass p): up to 16
+// of e's (token, slot) pairs, in order -- times 64-row tiles of the output;
+// a tile's contraction is split into stages of KS K-steps.  The grid is
+// persistent (two workgroups per CU); workgroup b takes the contiguous tiles
+// [b N / G, (b + 1) N / G), so consecutive tiles mostly share an item and its
+// staged token rows.  The stages of a workgroup form one software pipeline
+// over two register buffers: the weights of stage g + 1 are issued before
+// the MFMAs of stage g, so a wave always has about one tile of weights in
+// flight and HBM sees a steady stream instead of one burst per workgroup.
+struct ItemState {
+  int e, p, mcnt;
+  double tscale;
+  bool ok;
+};
+
+// The expert of item `it`: the e with pre[e] <= it < pre[e + 1].
+__device__ __forceinline__ int expert_of(const int* pre, int E, int it) {
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid] <= it) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+template <int FMT, int MODE, int KS>
+__global__ __launch_bounds__(64 * kBW, 2) void k_bat_gemm(BatchedArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   constexpr int NMAT = MODE == 0 ? 2 : 1;
+  constexpr int G = FMT == MOE_SCALE_E4M3_G16 ? 16 : 32;
+  constexpr int NLOADS = 3 * KS * NMAT;  // vector loads of one stage, per lane
   const int Kd = MODE == 0 ? a.H : a.I;
+  const int Nd = MODE == 0 ? a.I : a.H;
+  const int ntiles = Nd / kBN, nst = Kd / (kKS * KS);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int ln = lane & 15, g = lane >> 4;
-  lds_barrier();  // every wave's A rows are in LDS
-  if (MODE == 0) {
-    const bool prenorm = (a.flags & MOE_FLAG_PRENORM) != 0;
-    for (int r = wave; r < mcnt; r += kBW) {
-      uint16_t* row = xs + r * ldx;
-      if (prenorm) {
-        double ss = 0.0;
-        for (int k = lane; k < Kd; k += 64) {
-          const double f = bf2f(row[k]);
-          ss += f * f;
-        }
-        ss = seg_finish<32, double>(ss, lane);
-        const double rs = 1.0 / sqrt(ss / (double)Kd + (double)a.eps);
-        for (int k = lane; k < Kd; k += 64) row[k] = f64_to_bf16((double)bf2f(row[k]) * rs);
-      }
-      if (a.du && tile == 0) {
-        const int t = lp[r] / a.K;
-        for (int k = lane; k < Kd; k += 64) a.du[(size_t)t * Kd + k] = row[k];
+  const int ln = lane & 15, gl = lane >> 4;
+  const int ldx = Kd + 8;  // +16 B per row: conflict-free A reads
+  uint16_t* xs = lds;                   // [kMC][ldx]
+  int* list = (int*)(lds + kMC * ldx);  // [kMC]
+  int* cnt = list + kMC;                // [E]
+  int* pre = cnt + a.E;                 // [E + 1]: passes of the experts before e
+  int* wcnt = pre + a.E + 1;            // [kBW]
+  // the expert tables, staged once: weight bases, scale bases, tensor scales
+  const int tab_off = (kMC * ldx * 2 + (kMC + 2 * a.E + 1 + kBW) * 4 + 7) & ~7;  // bytes
+  const uint8_t** tw = (const uint8_t**)((char*)lds + tab_off);
+  const uint8_t** ts = tw + a.E;
+  float* tt = (float*)(ts + a.E);
+  const int npairs = a.T * a.K;
+
+  // 1. the items: per-expert pair counts, then the prefix of their passes
+  for (int e = tid; e < a.E; e += 64 * kBW) {
+    cnt[e] = 0;
+    tw[e] = a.wtab[e];
+    ts[e] = a.stab[e];
+    tt[e] = FMT == MOE_SCALE_E4M3_G16 ? a.tsc[2 * e + MODE] : 1.f;
+  }
+  __syncthreads();
+  bool bad = false;
+  const int id0 = tid < npairs ? a.ids[tid] : -1;
+  for (int p = tid; p < npairs; p += 64 * kBW) {
+    const int e = p == tid ? id0 : a.ids[p];
+    if ((unsigned)e < (unsigned)a.E) atomicAdd(&cnt[e], 1);
+    else bad = true;
+  }
+  if (MODE == 0 && blockIdx.x == 0 && bad && (a.flags & MOE_FLAG_CHECK_IDS)) atomicOr(a.err, kErrBadId);
+  __syncthreads();
+  auto aligned = [&](int e) {
+    return !(a.flags & MOE_FLAG_CHECK_IDS) || ((((uintptr_t)tw[e]) | ((uintptr_t)ts[e])) & 15u) == 0;
+  };
+  // a selected expert with a misaligned base is reported once and skipped
+  if (blockIdx.x == 0)
+    for (int e = tid; e < a.E; e += 64 * kBW)
+      if (cnt[e] > 0 && !aligned(e)) atomicOr(a.err, kErrAlign);
+  if (wave == 0) {
+    const int per = (a.E + 63) / 64;
+    int mine = 0;
+    for (int i = 0; i < per; ++i) {
+      const int e = lane * per + i;
+      if (e < a.E) mine += (cnt[e] + kMC - 1) / kMC;
+    }
+    int incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    int run = incl - mine;
+    for (int i = 0; i < per; ++i) {
+      const int e = lane * per + i;
+      if (e < a.E) {
+        pre[e] = run;
+        run += (cnt[e] + kMC - 1) / kMC;
       }
     }
-    if (prenorm) lds_barrier();
+    if (lane == 63) pre[a.E] = incl;
   }
+  __syncthreads();
+  const long long ntot = (long long)pre[a.E] * ntiles;
+  const int t0 = (int)(ntot * blockIdx.x / gridDim.x);
+  const int t1 = (int)(ntot * (blockIdx.x + 1) / gridDim.x);
+  if (t0 >= t1) return;
 
+  ItemState it;  // the item being computed
+  const uint8_t* wrow[2];
+  const uint8_t* srow[2];
+  const size_t rowb = (size_t)Kd / 2, rows = (size_t)Kd / G;
+  // the item whose weights were issued last; at an item change its first
+  // stage is issued before the old item's last stage is computed
+  int iss_item = -1;
+  const uint8_t* iw = nullptr;
+  const uint8_t* isc = nullptr;
+  bool iok = true;
+
+  // a new item: its expert, pass and pairs, then its token rows (direct
+  // loads, waited for later)
+  auto setup_item = [&](int item) {
+    const int e = expert_of(pre, a.E, item);
+    it.e = e;
+    it.p = item - pre[e];
+    it.mcnt = min(kMC, cnt[e] - kMC * it.p);
+    it.tscale = (double)tt[e];
+    it.ok = aligned(e);
+    collect_pairs(a.ids, id0, npairs, e, kMC * it.p, list, wcnt);
+    stage_rows<MODE>(a, list, it.mcnt, Kd, ldx, xs, wave, lane);
+  };
+  // row pointers of this lane for tile column block j of the current item
+  auto rows_for = [&](int j) {
+    const int n = j * kBN + wave * 16 + ln;
+    const size_t nn = iok ? (size_t)n : 0;
+    if (MODE == 0) {
+      wrow[0] = iw + nn * rowb;
+      wrow[1] = wrow[0] + (iok ? (size_t)a.I * rowb : 0);
+      srow[0] = isc + nn * rows;
+      srow[1] = srow[0] + (iok ? (size_t)a.I * rows : 0);
+    } else {
+      wrow[0] = wrow[1] = iw + (iok ? (size_t)a.I * a.H + nn * rowb : 0);
+      srow[0] = srow[1] = isc + (iok ? 2 * (size_t)a.I * (a.H / G) + nn * rows : 0);
+    }
+  };
+  auto issue = [&](WStep<FMT, NMAT>(&W)[KS], int g) {
+    const int tile = g / nst, st = g - tile * nst;
+    if (tile / ntiles != iss_item) {
+      iss_item = tile / ntiles;
+      const int e = expert_of(pre, a.E, iss_item);
+      iok = aligned(e);
+      // a rejected expert reads a harmless buffer: every step its first 36 bytes
+      iw = iok ? tw[e] : (const uint8_t*)a.x;
+      isc = iok ? ts[e] : (const uint8_t*)a.x;
+    }
+    rows_for(tile % ntiles);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) load_wstep<FMT, NMAT>(W[ks], wrow, srow, st * KS + ks, gl, iok);
+  };
+  // after the token rows of a new item have landed: pre-norm and dumps
+  auto rows_ready = [&](int first_tile) {
+    lds_barrier();  // every wave's token rows are in LDS
+    if (MODE == 0) {
+      const bool prenorm = (a.flags & MOE_FLAG_PRENORM) != 0;
+      const bool dump = a.du && first_tile % ntiles == 0;
+      for (int r = wave; r < it.mcnt; r += kBW) {
+        uint16_t* row = xs + r * ldx;
+        if (prenorm) {
+          double ss = 0.0;
+          for (int k = lane; k < Kd; k += 64) {
+            const double f = bf2f(row[k]);
+            ss += f * f;
+          }
+          ss = seg_finish<32, double>(ss, lane);
+          const double rs = 1.0 / sqrt(ss / (double)Kd + (double)a.eps);
+          for (int k = lane; k < Kd; k += 64) row[k] = f64_to_bf16((double)bf2f(row[k]) * rs);
+        }
+        if (dump) {
+          const int t = list[r] / a.K;
+          for (int k = lane; k < Kd; k += 64) a.du[(size_t)t * Kd + k] = row[k];
+        }
+      }
+      if (prenorm) lds_barrier();
+    }
+  };
   double acc[2][4];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[mt][i] = 0.0;
-  const uint16_t* arow = xs + ln * ldx + 64 * g;
-  for (int kb = 0; kb < nkb; ++kb) {
-    if (kb > 0) {
+  auto compute = [&](const WStep<FMT, NMAT>(&W)[KS], int g) {
+    const int tile = g / nst, st = g - tile * nst;
+    const uint16_t* arow = xs + ln * ldx + 64 * gl + st * KS * kKS;
 #pragma unroll
-      for (int ks = 0; ks < KB; ++ks) load_wstep<FMT, NMAT>(W[ks], wrow, srow, kb * KB + ks, g);
+    for (int ks = 0; ks < KS; ++ks) wstep_mfma<FMT, NMAT>(W[ks], arow + ks * kKS, acc);
+    if (st != nst - 1) return;
+    // epilogue: lane holds D[m = 4 gl + i][n] of the M tile
+    const int n = (tile % ntiles) * kBN + wave * 16 + ln;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * gl + i;
+      if (m < it.mcnt && it.ok) {
+        const int pair = list[m];
+        if (MODE == 0) {
+          const uint16_t gb = f64_to_bf16(acc[0][i] * it.tscale);
+          const uint16_t ub = f64_to_bf16(acc[1][i] * it.tscale);
+          const uint16_t h = silu_mul_bf16(gb, ub);
+          const size_t o = (size_t)pair * a.I + n;
+          a.hbuf[o] = h;
+          if (a.dg) a.dg[o] = gb;
+          if (a.dv) a.dv[o] = ub;
+          if (a.dh) a.dh[o] = h;
+        } else {
+          const uint16_t y = f64_to_bf16(acc[0][i] * it.tscale);
+          const size_t o = (size_t)pair * a.H + n;
+          a.ybuf[o] = y;
+          if (a.dy) a.dy[o] = y;
+        }
+      }
     }
 #pragma unroll
-    for (int ks = 0; ks < KB; ++ks) wstep_mfma<FMT, NMAT>(W[ks], arow + (kb * KB + ks) * kKS, acc);
-  }
-
-  // epilogue: lane holds D[m = 4g + i][n] of the M tile
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = 4 * g + i;
-    if (m >= mcnt) continue;
-    const int pair = lp[m];
-    if (MODE == 0) {
-      const uint16_t gb = f64_to_bf16(acc[0][i] * tscale);
-      const uint16_t ub = f64_to_bf16(acc[1][i] * tscale);
-      const uint16_t h = silu_mul_bf16(gb, ub);
-      const size_t o = (size_t)pair * a.I + n;
-      a.hbuf[o] = h;
-      if (a.dg) a.dg[o] = gb;
-      if (a.dv) a.dv[o] = ub;
-      if (a.dh) a.dh[o] = h;
-    } else {
-      const uint16_t y = f64_to_bf16(acc[0][i] * tscale);
-      const size_t o = (size_t)pair * a.H + n;
-      a.ybuf[o] = y;
-      if (a.dy) a.dy[o] = y;
+      for (int i = 0; i < 4; ++i) acc[mt][i] = 0.0;
+  };
+
+  // 2. the pipeline.  W0 and W1 alternate: before a stage is computed, the
+  // other buffer's next stage -- the next item's first one at an item change;
+  // the same stage again, a harmless L2 re-read, at the end of the range --
+  // has been issued after it, so every path reaches each MFMA with one stage
+  // of loads in flight and the compiler's wait counts stay exact.  A new item
+  // finds its pairs and starts its token rows while its first stage is
+  // already in flight.
+  WStep<FMT, NMAT> W0[KS], W1[KS];
+  int g = t0 * nst;
+  const int gend = t1 * nst;
+  auto item_of = [&](int gg) { return gg / nst / ntiles; };
+  auto next = [&](int gg) { return gg + 1 < gend ? gg + 1 : gg; };
+  issue(W0, g);
+  setup_item(item_of(g));
+  __builtin_amdgcn_sched_barrier(0);
+  issue(W1, next(g));
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vm<NLOADS>();  // the token rows (and stage g) have landed
+  rows_ready(g / nst);
+  // One issue site per buffer: paths that loaded a buffer in different code
+  // would meet in register copies, which wait for the loads in flight.  At an
+  // item change the token rows are waited for with everything older before
+  // the next stage is issued: with direct-to-LDS loads possibly in flight the
+  // compiler would otherwise wait for all loads before every LDS read.
+  for (;;) {
+    compute(W0, g);
+    if (++g >= gend) break;
+    bool change = item_of(g) != item_of(g - 1);
+    if (change) {
+      lds_barrier();  // the old item's rows and pairs are no longer read
+      setup_item(item_of(g));
+      wait_vm<0>();  // the token rows (and W1, issued a stage ago) have landed
     }
-  }
-}
-
-// MODE 0: A = x rows (pre-normed if asked), B = gate and up -> h.
-// MODE 1: A = h rows, B = down -> y.   KB = K steps held in registers; when
-// they do not cover the contraction, blocks of KB steps follow in turn.
-template <int FMT, int MODE, int KB>
-__global__ __launch_bounds__(64 * kBW, 2) void k_bat_gemm(BatchedArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  constexpr int NMAT = MODE == 0 ? 2 : 1;
-  constexpr int G = FMT == MOE_SCALE_E4M3_G16 ? 16 : 32;
-  const int Kd = MODE == 0 ? a.H : a.I;
-  const int Nd = MODE == 0 ? a.I : a.H;
-  const int ntiles = Nd / kBN;
-  const int e = blockIdx.x / ntiles, tile = blockIdx.x % ntiles;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int ln = lane & 15, g = lane >> 4;
-  const int n = tile * kBN + wave * 16 + ln;  // this lane's output row (B column)
-  const int ldx = Kd + 8;                     // +16 B per row: conflict-free A reads
-  uint16_t* xs = lds;                         // [kMC][ldx]
-  int* list = (int*)(lds + kMC * ldx);        // [kListCap]
-  int* wcnt = list + kListCap;                 // [kBW]
-  const int npairs = a.T * a.K;
-  // Read before any store so that they become scalar loads: a vector load
-  // still in flight when the direct LDS loads below are issued would make
-  // the compiler wait for every one of those before the weight loads.
-  const uint8_t* wb = a.wtab[e];
-  const uint8_t* sb = a.stab[e];
-  double tscale = 1.0;
-  if constexpr (FMT == MOE_SCALE_E4M3_G16) tscale = (double)a.tsc[2 * e + MODE];
-
-  // 1. this expert's pairs (ids outside [0, E) match no expert: their y
-  //    stays as the caller cleared it; one workgroup reports them)
-  if (MODE == 0 && blockIdx.x == 0 && (a.flags & MOE_FLAG_CHECK_IDS)) {
-    bool bad = false;
-    for (int p = tid; p < npairs; p += 64 * kBW) bad |= (unsigned)a.ids[p] >= (unsigned)a.E;
-    if (bad) atomicOr(a.err, kErrBadId);
-  }
-  const int M = collect_pairs(a.ids, npairs, e, 0, list, wcnt);
-  if (M == 0) return;
-
-  if ((a.flags & MOE_FLAG_CHECK_IDS) && ((((uintptr_t)wb) | ((uintptr_t)sb)) & 15u)) {
-    if (tid == 0) atomicOr(a.err, kErrAlign);
-    return;  // its pairs keep y = 0 (the caller clears y under this flag)
-  }
-  const size_t rowb = (size_t)Kd / 2, rows = (size_t)Kd / G;
-  const uint8_t* wrow[2];
-  const uint8_t* srow[2];
-  if (MODE == 0) {
-    wrow[0] = wb + n * rowb;
-    wrow[1] = wrow[0] + (size_t)a.I * rowb;
-    srow[0] = sb + n * rows;
-    srow[1] = srow[0] + (size_t)a.I * rows;
-  } else {
-    wrow[0] = wrow[1] = wb + (size_t)a.I * a.H + n * rowb;
-    srow[0] = srow[1] = sb + 2 * (size_t)a.I * (a.H / G) + n * rows;
-  }
-  const int nkb = Kd / (kKS * KB);
-
-  // 2. per 16-token pass: the A rows go straight from global memory (L2) into
-  //    LDS, then the first KB steps of weights are issued; loads retire in
-  //    issue order, so the wait for this wave's A rows leaves the weight loads
-  //    in flight.  The first pass is peeled off the loop: with the weight loads
-  //    outside a loop nothing computed from them is hoisted ahead of the A
-  //    staging (which would wait for them).  Later passes (experts with more
-  //    than 16 tokens) re-read the weights, from L2.
-  WStep<FMT, NMAT> W[KB];
-  int mcnt = min(kMC, M);
-  stage_rows<MODE>(a, list, mcnt, Kd, ldx, xs, wave, lane);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int ks = 0; ks < KB; ++ks) load_wstep<FMT, NMAT>(W[ks], wrow, srow, ks, g);
-  __builtin_amdgcn_sched_barrier(0);
-  wait_vm<3 * KB * NMAT>();
-  gemm_pass<FMT, MODE, KB>(a, W, wrow, srow, xs, ldx, list, mcnt, nkb, n, tile, tscale);
-  for (int c0 = kMC; c0 < M; c0 += kMC) {
-    lds_barrier();  // the previous pass has read xs and its pair indices
-    if (c0 % kListCap == 0) collect_pairs(a.ids, npairs, e, c0, list, wcnt);
-    const int* lp = list + (c0 % kListCap);
-    mcnt = min(kMC, M - c0);
-    stage_rows<MODE>(a, lp, mcnt, Kd, ldx, xs, wave, lane);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 0; ks < KB; ++ks) load_wstep<FMT, NMAT>(W[ks], wrow, srow, ks, g);
+    issue(W0, next(g));
+    __builtin_amdgcn_sched_barrier(0);  // no use of W1 above these loads
+    if (change) rows_ready(g / nst);
+    compute(W1, g);
+    if (++g >= gend) break;
+    change = item_of(g) != item_of(g - 1);
+    if (change) {
+      lds_barrier();
+      setup_item(item_of(g));
+      wait_vm<0>();
+    }
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm<3 * KB * NMAT>();
-    gemm_pass<FMT, MODE, KB>(a, W, wrow, srow, xs, ldx, lp, mcnt, nkb, n, tile, tscale);
+    issue(W1, next(g));
+    __builtin_amdgcn_sched_barrier(0);
+    if (change) rows_ready(g / nst);
   }
 }
 
@@ -444,41 +559,58 @@ hipError_t allow_lds(KernelT kernel, size_t bytes) {
                              (int)bytes);
 }
 
-template <int FMT, int MODE, int KB>
-hipError_t launch_gemm_kb(const BatchedArgs& a, hipStream_t s) {
-  const int Kd = MODE == 0 ? a.H : a.I, Nd = MODE == 0 ? a.I : a.H;
-  const size_t lds = (size_t)kMC * (Kd + 8) * 2 + (size_t)(kListCap + kBW) * 4;
-  // The largest contraction a shape check admits (4096) needs 136.3 KiB.
+int cu_count() {
+  static int n = 0;  // benign race: every caller computes the same value
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
+template <int FMT, int MODE, int KS>
+hipError_t launch_gemm_ks(const BatchedArgs& a, hipStream_t s) {
+  const int Kd = MODE == 0 ? a.H : a.I;
+  const size_t lds = (size_t)kMC * (Kd + 8) * 2 + (size_t)(kMC + 2 * a.E + 1 + kBW) * 4 + 8 +
+                     (size_t)a.E * (2 * sizeof(void*) + sizeof(float));
+  // The largest shape a check admits (K 4096, 1024 experts) needs 156.3 KiB.
   static size_t allowed = 0;  // benign race: the value only grows towards the same bound
   if (lds > allowed) {
-    hipError_t e = allow_lds(k_bat_gemm<FMT, MODE, KB>, lds);
+    hipError_t e = allow_lds(k_bat_gemm<FMT, MODE, KS>, lds);
     if (e != hipSuccess) return e;
     allowed = lds;
   }
   return launch_kernel(MODE == 0 ? MOE_KERNEL_BATCHED_GATE_UP : MOE_KERNEL_BATCHED_DOWN,
-                       k_bat_gemm<FMT, MODE, KB>, dim3(a.E * (Nd / kBN)), dim3(64 * kBW), lds, s, a);
+                       k_bat_gemm<FMT, MODE, KS>, dim3(2 * cu_count()), dim3(64 * kBW), lds, s, a);
 }
 
-// Up to 8 K steps (2048 contraction elements) stay in registers for the whole
-// call; longer contractions go in blocks of 8, 4, 2 or 1 steps.
+// K steps per pipeline stage: the largest divisor of the step count up to 2
+// (gate and up: two matrices) or 8 (down), so that two stages of weights fit
+// in registers next to each other without spilling.
 template <int FMT, int MODE>
 hipError_t launch_gemm(const BatchedArgs& a, hipStream_t s) {
   const int nks = (MODE == 0 ? a.H : a.I) / kKS;
-  switch (nks) {
-    case 1: return launch_gemm_kb<FMT, MODE, 1>(a, s);
-    case 2: return launch_gemm_kb<FMT, MODE, 2>(a, s);
-    case 3: return launch_gemm_kb<FMT, MODE, 3>(a, s);
-    case 4: return launch_gemm_kb<FMT, MODE, 4>(a, s);
-    case 5: return launch_gemm_kb<FMT, MODE, 5>(a, s);
-    case 6: return launch_gemm_kb<FMT, MODE, 6>(a, s);
-    case 7: return launch_gemm_kb<FMT, MODE, 7>(a, s);
-    case 8: return launch_gemm_kb<FMT, MODE, 8>(a, s);
-    default: break;
+  const int cap = MODE == 0 ? 2 : 8;
+  int ks = 1;
+  for (int d = cap; d >= 1; --d)
+    if (nks % d == 0) {
+      ks = d;
+      break;
+    }
+  switch (ks) {
+    case 8: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 2 : 8)>(a, s);
+    case 7: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 1 : 7)>(a, s);
+    case 6: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 2 : 6)>(a, s);
+    case 5: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 1 : 5)>(a, s);
+    case 4: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 2 : 4)>(a, s);
+    case 3: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 1 : 3)>(a, s);
+    case 2: return launch_gemm_ks<FMT, MODE, 2>(a, s);
+    default: return launch_gemm_ks<FMT, MODE, 1>(a, s);
   }
-  if (nks % 8 == 0) return launch_gemm_kb<FMT, MODE, 8>(a, s);
-  if (nks % 4 == 0) return launch_gemm_kb<FMT, MODE, 4>(a, s);
-  if (nks % 2 == 0) return launch_gemm_kb<FMT, MODE, 2>(a, s);
-  return launch_gemm_kb<FMT, MODE, 1>(a, s);
 }
 
 template <int FMT>
