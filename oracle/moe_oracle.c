@@ -38,6 +38,11 @@
  * value.  Sums run sequentially in fp64 with k ascending.  Build with
  * -O2 -ffp-contract=off and no fast-math, so no FMA changes any rounding.
  *
+ * W4A4 variant ([NVFP4 card], "Why this quant": the W4A4 builds quantise the
+ * expert activations to 4 bits as well, for FP4 matrix hardware): u and every
+ * h are replaced by their MXFP4 quantisation (see oracle_quant_mxfp4) before
+ * the GEMV that consumes them; everything else is unchanged.
+ *
  * Readings where the pages are silent (each is listed with its reason in the
  * design notes): low nibble = even k; scale blocks aligned at k = 0 along a
  * row; matrices stored [out][in] row-major; one rounding inside silu*up;
@@ -252,6 +257,74 @@ int oracle_sort_pairs(const int32_t* ids, int T, int K, int E,
 }
 
 /* ---------------------------------------------------------------------- */
+/* 4-bit activations (W4A4)                                                */
+/* ---------------------------------------------------------------------- */
+
+/* MXFP4 quantisation of activations.  [NVFP4 card], "Why this quant", says
+ * only that the W4A4 builds make the expert activations 4-bit; it gives no
+ * format.  Reading: the weights' own format ([MXFP4 card], "Model and
+ * quantization": E2M1 values, two per byte, one E8M0 scale per 32 values
+ * along k), with the shared-scale rule and element conversion of the OCP
+ * Microscaling (MX) Formats specification v1.0, section "Conversion":
+ *   X   = 2^(floor(log2(max |v|)) - 2) per block of 32 (2 is the largest
+ *         E2M1 exponent), the exponent clamped to -127..127; a block of zeros
+ *         takes X = 2^-127 (E8M0 code 0);
+ *   q_i = v_i / X rounded to E2M1, nearest with ties to the even code,
+ *         magnitudes beyond 6 saturating to 6; the sign bit is the input's.
+ * The quantised activation is q_i * X.  E2M1 keeps one mantissa bit, so the
+ * step is 0.5 below 2, 1 in [2, 4) and 2 from 4 up.
+ * v [rows][cols] bf16; codes [rows][cols/2] (low nibble = even k, as the
+ * weights); scales [rows][cols/32] E8M0.  Returns -1 unless cols % 32 == 0. */
+int oracle_quant_mxfp4(const uint16_t* v, int rows, int cols, uint8_t* codes, uint8_t* scales)
+{
+    if (rows < 0 || cols <= 0 || cols % 32 != 0) return -1;
+    for (int r = 0; r < rows; ++r)
+        for (int b = 0; b < cols / 32; ++b) {
+            const uint16_t* blk = v + (size_t)r * cols + 32 * b;
+            double amax = 0.0;
+            for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(oracle_f64_from_bf16(blk[i])));
+            int x = -127;
+            if (amax > 0.0) {
+                int ex;
+                frexp(amax, &ex);          /* amax in [2^(ex-1), 2^ex) */
+                x = (ex - 1) - 2;
+                if (x < -127) x = -127;
+                if (x > 127) x = 127;
+            }
+            scales[(size_t)r * (cols / 32) + b] = (uint8_t)(x + 127);
+            for (int i = 0; i < 32; ++i) {
+                double val = oracle_f64_from_bf16(blk[i]);
+                double a = ldexp(fabs(val), -x);                 /* exact */
+                double step = a < 2.0 ? 0.5 : (a < 4.0 ? 1.0 : 2.0);
+                double q = round_half_even(a / step) * step;
+                if (q > 6.0) q = 6.0;
+                int code = 0;
+                while (E2M1_TABLE[code] != q) ++code;            /* q is on the grid */
+                if (signbit(val)) code |= 8;
+                const int k = 32 * b + i;
+                uint8_t* byte = codes + (size_t)r * (cols / 2) + k / 2;
+                if (k & 1) *byte = (uint8_t)((*byte & 0x0F) | (code << 4));
+                else *byte = (uint8_t)((*byte & 0xF0) | code);
+            }
+        }
+    return 0;
+}
+
+/* The quantised values of one row as fp64: q_i * X (exact). */
+static void quant_row_values(const uint16_t* v, int cols, double* out)
+{
+    uint8_t* c = (uint8_t*)calloc((size_t)cols / 2, 1);
+    uint8_t* s = (uint8_t*)malloc((size_t)cols / 32);
+    oracle_quant_mxfp4(v, 1, cols, c, s);
+    for (int k = 0; k < cols; ++k) {
+        int code = (k & 1) ? (c[k / 2] >> 4) : (c[k / 2] & 15);
+        out[k] = E2M1_TABLE[code] * oracle_e8m0(s[k / 32]);
+    }
+    free(c);
+    free(s);
+}
+
+/* ---------------------------------------------------------------------- */
 /* The whole layer                                                         */
 /* ---------------------------------------------------------------------- */
 
@@ -265,18 +338,19 @@ int oracle_sort_pairs(const int32_t* ids, int T, int K, int E,
  * dump_*   optional: u [T][H], g/v/h [T][K][I], y [T][K][H] (bf16)
  * Returns 0, or -1 on a bad argument.
  */
-int oracle_moe_forward(int T, int H, int I, int E, int K, int fmt,
-                       const uint16_t* x, const int32_t* ids, const uint16_t* route_w,
-                       const uint8_t* const* nib, const uint8_t* const* scl,
-                       const float* tscales, const uint16_t* residual,
-                       int prenorm, double eps, uint16_t* out,
-                       uint16_t* dump_u, uint16_t* dump_g, uint16_t* dump_v,
-                       uint16_t* dump_h, uint16_t* dump_y, int nthreads)
+static int moe_forward_impl(int T, int H, int I, int E, int K, int fmt,
+                            const uint16_t* x, const int32_t* ids, const uint16_t* route_w,
+                            const uint8_t* const* nib, const uint8_t* const* scl,
+                            const float* tscales, const uint16_t* residual,
+                            int prenorm, double eps, uint16_t* out,
+                            uint16_t* dump_u, uint16_t* dump_g, uint16_t* dump_v,
+                            uint16_t* dump_h, uint16_t* dump_y, int nthreads, int a4)
 {
     if (T < 0 || H <= 0 || I <= 0 || E <= 0 || K <= 0) return -1;
     if (fmt != ORC_FMT_E8M0_G32 && fmt != ORC_FMT_E4M3_G16) return -1;
     int G = group_of(fmt);
     if (H % G || I % G || H % 2 || I % 2) return -1;
+    if (a4 && (fmt != ORC_FMT_E8M0_G32 || H % 32 || I % 32)) return -1;
     for (int p = 0; p < T * K; ++p)
         if (ids[p] < 0 || ids[p] >= E) return -1;
 #ifdef _OPENMP
@@ -300,7 +374,9 @@ int oracle_moe_forward(int T, int H, int I, int E, int K, int fmt,
         const uint16_t* xt = x + (size_t)t * H;
         if (prenorm) oracle_prenorm(xt, ub, H, eps);
         else memcpy(ub, xt, sizeof(uint16_t) * (size_t)H);
-        for (int k = 0; k < H; ++k) uv[k] = oracle_f64_from_bf16(ub[k]);
+        if (a4) quant_row_values(ub, H, uv);
+        else
+            for (int k = 0; k < H; ++k) uv[k] = oracle_f64_from_bf16(ub[k]);
         if (dump_u) memcpy(dump_u + (size_t)t * H, ub, sizeof(uint16_t) * (size_t)H);
 
         /* gate, up, silu*up for every slot */
@@ -321,6 +397,8 @@ int oracle_moe_forward(int T, int H, int I, int E, int K, int fmt,
                 if (dump_v) dump_v[d] = vb;
                 if (dump_h) dump_h[d] = h;
             }
+        if (a4)
+            for (int j = 0; j < K; ++j) quant_row_values(hb + (size_t)j * I, I, hv + (size_t)j * I);
         /* down */
 #pragma omp parallel for collapse(2) schedule(static)
         for (int j = 0; j < K; ++j)
@@ -337,6 +415,36 @@ int oracle_moe_forward(int T, int H, int I, int E, int K, int fmt,
     }
     free(ub); free(uv); free(hb); free(hv); free(yb);
     return 0;
+}
+
+int oracle_moe_forward(int T, int H, int I, int E, int K, int fmt,
+                       const uint16_t* x, const int32_t* ids, const uint16_t* route_w,
+                       const uint8_t* const* nib, const uint8_t* const* scl,
+                       const float* tscales, const uint16_t* residual,
+                       int prenorm, double eps, uint16_t* out,
+                       uint16_t* dump_u, uint16_t* dump_g, uint16_t* dump_v,
+                       uint16_t* dump_h, uint16_t* dump_y, int nthreads)
+{
+    return moe_forward_impl(T, H, I, E, K, fmt, x, ids, route_w, nib, scl, tscales, residual,
+                            prenorm, eps, out, dump_u, dump_g, dump_v, dump_h, dump_y,
+                            nthreads, 0);
+}
+
+/* The W4A4 layer: as oracle_moe_forward, with u and every h replaced by their
+ * MXFP4 quantisation before the GEMV that reads them.  MXFP4 weights only
+ * (the E8M0 block scale of the activations and the weights must agree in
+ * kind for FP4 matrix hardware); returns -1 for the E4M3 format. */
+int oracle_moe_forward_w4a4(int T, int H, int I, int E, int K, int fmt,
+                            const uint16_t* x, const int32_t* ids, const uint16_t* route_w,
+                            const uint8_t* const* nib, const uint8_t* const* scl,
+                            const float* tscales, const uint16_t* residual,
+                            int prenorm, double eps, uint16_t* out,
+                            uint16_t* dump_u, uint16_t* dump_g, uint16_t* dump_v,
+                            uint16_t* dump_h, uint16_t* dump_y, int nthreads)
+{
+    return moe_forward_impl(T, H, I, E, K, fmt, x, ids, route_w, nib, scl, tscales, residual,
+                            prenorm, eps, out, dump_u, dump_g, dump_v, dump_h, dump_y,
+                            nthreads, 1);
 }
 
 /* ---------------------------------------------------------------------- */

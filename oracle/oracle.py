@@ -60,6 +60,10 @@ def _declare(L):
     L.oracle_moe_forward.argtypes = [
         C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
         P, P, P, P, P, P, P, C.c_int, C.c_double, P, P, P, P, P, P, C.c_int]
+    L.oracle_moe_forward_w4a4.restype = C.c_int
+    L.oracle_moe_forward_w4a4.argtypes = L.oracle_moe_forward.argtypes
+    L.oracle_quant_mxfp4.restype = C.c_int
+    L.oracle_quant_mxfp4.argtypes = [P, C.c_int, C.c_int, P, P]
     L.oracle_threads_available.restype = C.c_int
     L.oracle_threads_available.argtypes = []
     L.oracle_route.restype = C.c_int
@@ -148,14 +152,30 @@ def sort_pairs(ids, num_experts: int):
     return counts, offsets, perm
 
 
+def quant_mxfp4(v):
+    """MXFP4 quantisation of BF16 rows (see oracle_quant_mxfp4): v [rows][cols]
+    BF16 bits -> (codes [rows][cols/2] uint8, low nibble = even k;
+    scales [rows][cols/32] E8M0 uint8)."""
+    v = _c(v, np.uint16)
+    if v.ndim == 1:
+        v = v[None, :]
+    rows, cols = v.shape
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.zeros((rows, cols // 32), np.uint8)
+    if lib().oracle_quant_mxfp4(_ptr(v), rows, cols, _ptr(codes), _ptr(scales)) != 0:
+        raise ValueError("oracle_quant_mxfp4: cols must be a multiple of 32")
+    return codes, scales
+
+
 def threads_available() -> int:
     return lib().oracle_threads_available()
 
 
 def moe_forward(x, ids, route_w, nibbles, scales, *, hidden, inter, num_experts, fmt,
                 tensor_scales=None, residual=None, prenorm=False, eps=1e-5,
-                dumps=False, nthreads=0):
-    """One MoE layer on the CPU.
+                dumps=False, nthreads=0, w4a4=False):
+    """One MoE layer on the CPU (the W4A4 layer when ``w4a4``: activations
+    quantised to MXFP4 before each GEMV, MXFP4 weights only).
 
     x [T][H] bf16 bits; ids [T][K] int32; route_w [T][K] bf16 bits;
     nibbles / scales: sequences (length E) of per-expert uint8 arrays, or None
@@ -192,7 +212,8 @@ def moe_forward(x, ids, route_w, nibbles, scales, *, hidden, inter, num_experts,
         d = {"u": np.empty((T, H), np.uint16), "g": np.empty((T, K, I), np.uint16),
              "v": np.empty((T, K, I), np.uint16), "h": np.empty((T, K, I), np.uint16),
              "y": np.empty((T, K, H), np.uint16)}
-    rc = lib().oracle_moe_forward(
+    fn = lib().oracle_moe_forward_w4a4 if w4a4 else lib().oracle_moe_forward
+    rc = fn(
         T, H, I, E, K, fmt, _ptr(x), _ptr(ids), _ptr(w),
         C.cast(nib_tab, C.c_void_p), C.cast(sc_tab, C.c_void_p), _ptr(ts), _ptr(r),
         1 if prenorm else 0, float(eps), _ptr(out),

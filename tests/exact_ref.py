@@ -108,6 +108,52 @@ def silu_mul_bf16(g: F, u: F) -> F:
     return bf16_round(F(_CTX.multiply(s, _dec(u))))
 
 
+# -- MXFP4 activations (W4A4) ------------------------------------------------------
+# Reading of "primitive-ai/LFM2.5-24B-A2B-NVFP4A16" ("Why this quant": the W4A4
+# builds make the expert activations 4-bit): the weights' MXFP4 format of
+# "LFM2.5-24B-A2B -- Packed MXFP4 Inference" ("Model and quantization"), with
+# the OCP MX v1.0 shared scale 2^(floor(log2 amax) - 2) (exponent clamped to
+# -127..127, 2^-127 for a zero block) and nearest-E2M1 elements, ties to the
+# even code.  Here the nearest element is found by trying all eight
+# magnitudes on exact rationals, a different procedure from the oracle's.
+
+def mxfp4_quant_bits(bits: list) -> tuple:
+    """One block of 32 BF16 bit patterns -> (codes list, E8M0 scale code)."""
+    vals = [bf16_bits_value(b) for b in bits]
+    amax = max(abs(v) for v in vals)
+    x = -127 if amax == 0 else min(127, max(-127, _floor_log2(amax) - 2))
+    X = F(2) ** x
+    codes = []
+    for b, v in zip(bits, vals):
+        r = abs(v) / X
+        best = None
+        for c in range(8):
+            d = abs(e2m1(c) - r)
+            if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+                best = (d, c)
+        codes.append(best[1] | (8 if (int(b) >> 15) & 1 else 0))
+    return codes, x + 127
+
+
+def mxfp4_values(bits: list) -> list:
+    """Quantised values (exact) of a BF16 row whose length is a multiple of 32."""
+    out = []
+    for i in range(0, len(bits), 32):
+        codes, sc = mxfp4_quant_bits(bits[i:i + 32])
+        out += [e2m1(c) * e8m0(sc) for c in codes]
+    return out
+
+
+def signed_zero_product_bits(h: F, g: F, v: F) -> int:
+    """BF16 bits of h = silu(g) * v.  Exact rationals carry no sign of zero;
+    IEEE arithmetic gives a zero product the XOR of its factors' signs, with
+    silu(g) negative exactly when g is and every exact-zero sum being +0."""
+    if h != 0:
+        return bf16_bits(h)
+    neg = (g < 0) != (v < 0)
+    return 0x8000 if neg else 0
+
+
 # -- the layer ----------------------------------------------------------------------
 
 def _weight(nib: bytes, sc: bytes, cols: int, fmt: int, n: int, k: int, tscale: F) -> F:
@@ -127,15 +173,18 @@ def prenorm(x: list, eps: float) -> list:
 
 
 def layer(x_bits, ids, w_bits, nibbles, scales, H, I, fmt, tscales=None,
-          residual_bits=None, use_prenorm=False, eps=1e-5):
+          residual_bits=None, use_prenorm=False, eps=1e-5, w4a4=False):
     """Exact layer for tiny shapes.  Returns dict of BF16 bit-pattern lists:
-    out [T][H], u [T][H], g/v/h [T][K][I], y [T][K][H]."""
+    out [T][H], u [T][H], g/v/h [T][K][I], y [T][K][H].  With ``w4a4`` the
+    GEMVs read the MXFP4 quantisation of u and of each h."""
     T, K = len(ids), len(ids[0])
     res = {"out": [], "u": [], "g": [], "v": [], "h": [], "y": []}
     for t in range(T):
         x = [bf16_bits_value(b) for b in x_bits[t]]
         u = prenorm(x, eps) if use_prenorm else x
         res["u"].append([bf16_bits(v) for v in u])
+        if w4a4:
+            u = mxfp4_values(res["u"][-1])
         gs, vs, hs, ys = [], [], [], []
         for j in range(K):
             e = int(ids[t][j])
@@ -151,11 +200,13 @@ def layer(x_bits, ids, w_bits, nibbles, scales, H, I, fmt, tscales=None,
             v = [bf16_round(sum(u[k] * _weight(nib[up_n:], sc[up_s:], H, fmt, n, k, tg)
                                 for k in range(H))) for n in range(I)]
             h = [silu_mul_bf16(g[n], v[n]) for n in range(I)]
-            y = [bf16_round(sum(h[n] * _weight(nib[down_n:], sc[down_s:], I, fmt, m, n, td)
+            hbits = [signed_zero_product_bits(h[n], g[n], v[n]) for n in range(I)]
+            hq = mxfp4_values(hbits) if w4a4 else h
+            y = [bf16_round(sum(hq[n] * _weight(nib[down_n:], sc[down_s:], I, fmt, m, n, td)
                                 for n in range(I))) for m in range(H)]
             gs.append([bf16_bits(a) for a in g])
             vs.append([bf16_bits(a) for a in v])
-            hs.append([bf16_bits(a) for a in h])
+            hs.append(hbits)
             ys.append(y)
         out = []
         for m in range(H):
