@@ -35,7 +35,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=64)
     p.add_argument("--workload", default="c1",
                    choices=["c1", "c0", "c2", "c2stack", "c3", "c4", "c4b32", "c1serial",
-                            "c1routed"])
+                            "c1routed", "c2w4a4", "c3w4a4", "c2stackw4a4"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--calib", action="store_true",
@@ -70,10 +70,12 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     shape = S.LFM24B
-    wname = {"c2stack": "c2", "c1serial": "c1", "c1routed": "c1"}.get(args.workload, args.workload)
+    wname = {"c2stack": "c2", "c1serial": "c1", "c1routed": "c1", "c2w4a4": "c2", "c3w4a4": "c3",
+             "c2stackw4a4": "c2"}.get(args.workload, args.workload)
     routed = args.workload == "c1routed"
+    w4a4 = args.workload.endswith("w4a4")
     w = S.WORKLOADS[wname]
-    stack = args.workload in ("c1", "c2stack", "c1serial", "c1routed")
+    stack = args.workload in ("c1", "c2stack", "c1serial", "c1routed", "c2stackw4a4")
     T, E, K, H = w.tokens, shape.experts, shape.top_k, shape.hidden
     # layers resident: the whole 38-layer stack for every workload, so single-
     # layer workloads rotate over 38 layers and the reuse distance (762 MB+ per
@@ -110,8 +112,10 @@ def main():
                                            for l in range(L)])).to(dev)
     stream = torch.cuda.Stream()  # capture needs a non-default stream; every launch and event uses it
     torch.cuda.set_stream(stream)
-    cfg = M.make_cfg(T, H, shape.inter, E, K, w.fmt, prenorm_eps=EPS, stream=stream,
-                     flags=M.FLAG_SERIAL if args.workload == "c1serial" else 0)
+    flags = M.FLAG_SERIAL if args.workload == "c1serial" else 0
+    if w4a4:
+        flags |= M.FLAG_W4A4
+    cfg = M.make_cfg(T, H, shape.inter, E, K, w.fmt, prenorm_eps=EPS, stream=stream, flags=flags)
     if w.fmt == S.FMT_E4M3_G16:
         cfg.tensor_scales = store.tscales[0].data_ptr()
     ws = torch.zeros(M.moe_w4a16_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
@@ -233,7 +237,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, shape, args.cpu_seconds)
+        cpu = cpu_baseline(w, shape, args.cpu_seconds, w4a4=w4a4)
 
     if dominant is not None and "achieved_GBps" in dominant:
         roof = {"bound": "hbm", "achieved": dominant["achieved_GBps"], "peak": HBM_PEAK_GBPS,
@@ -245,7 +249,10 @@ def main():
         if dominant["_kind"] in (4, 5):
             fl = kernel_flops(shape, T, dominant["_kind"])
             roof["mfma_useful_TFLOPs"] = fl / (dominant["mean_us"] / 1e6) / 1e12
-            roof["mfma_useful_frac_of_bf16_peak"] = roof["mfma_useful_TFLOPs"] / 2500.0
+            if w4a4:  # E2M1 x E2M1 on the block-scaled FP4 MFMA: dense peak 10.1 PFLOP/s
+                roof["mfma_useful_frac_of_fp4_peak"] = roof["mfma_useful_TFLOPs"] / 10100.0
+            else:
+                roof["mfma_useful_frac_of_bf16_peak"] = roof["mfma_useful_TFLOPs"] / 2500.0
     else:
         roof = {"bound": "hbm", "achieved": achieved_step, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": achieved_step / HBM_PEAK_GBPS, "traffic": None, "kernel": "whole step"}
@@ -264,7 +271,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp4" if w4a4 else "bf16",
         "data": "synthetic (seeded E2M1 nibbles, E8M0 117..123 or E4M3 normal scales, x ~ N(0,1) BF16)",
         "config": {
             "workload": workload_name(args.workload),
@@ -417,10 +424,15 @@ def workload_name(k):
         "c3": "prefill: S=64 chunks through one layer (rotating over 38 layers)",
         "c4": "NVFP4-style E2M1+E4M3/16+FP32 tensor scale, batch 1",
         "c4b32": "NVFP4-style E2M1+E4M3/16+FP32 tensor scale, batch 32",
+        "c2w4a4": "concurrency-32 decode, one layer per call, W4A4 (MXFP4 activations on the "
+                  "block-scaled FP4 MFMA)",
+        "c3w4a4": "prefill S=64 chunks through one layer, W4A4 (MXFP4 activations on the "
+                  "block-scaled FP4 MFMA)",
+        "c2stackw4a4": "concurrency-32 decode through the 38-layer stack, W4A4",
     }[k]
 
 
-def cpu_baseline(w, shape, target_s):
+def cpu_baseline(w, shape, target_s, w4a4=False):
     """The oracle as it stands on this host's cores, on a bounded sample of the
     workload: layer calls of the workload's batch in the workload's order
     (consecutive layers of one step, chained through the pre-norm and residual
@@ -451,14 +463,15 @@ def cpu_baseline(w, shape, target_s):
         t0 = time.perf_counter()
         out = O.moe_forward(h, ids, rw, nib, sc, hidden=shape.hidden, inter=shape.inter,
                             num_experts=shape.experts, fmt=w.fmt, tensor_scales=ts,
-                            residual=h if w.chained else None, prenorm=w.chained, eps=EPS)
+                            residual=h if w.chained else None, prenorm=w.chained, eps=EPS,
+                            w4a4=w4a4)
         busy += time.perf_counter() - t0
         if w.chained:
             h = out
         calls += 1
     return {"value": T * calls / busy, "unit": "tokens/s per MoE layer", "cores": threads,
             "kind": "oracle",
-            "sample": f"{calls} layer calls of {T} token(s) on {w.name} inputs (layers 0..{min(calls, shape.layers) - 1}"
+            "sample": f"{calls} {'W4A4 ' if w4a4 else ''}layer calls of {T} token(s) on {w.name} inputs (layers 0..{min(calls, shape.layers) - 1}"
                       f"{', chained' if w.chained else ''}), fp64 scalar C oracle with {threads} OpenMP "
                       f"threads, {busy:.1f} s of oracle time (input generation excluded)"}
 

@@ -97,6 +97,18 @@ extern "C" {
  * and one combine launch follows (2k + 1 launches per layer instead of 2).
  * Same device functions, so the results equal the grouped path's bit for bit. */
 #define MOE_FLAG_SERIAL (1u << 4)
+/* W4A4: the expert activations are 4-bit as well ("primitive-ai/LFM2.5-24B-
+ * A2B-NVFP4A16", "Why this quant": the W4A4 builds quantise the expert
+ * activations too and run on FP4 matrix hardware).  u and every h are
+ * quantised to MXFP4 before the GEMV that reads them: per block of 32 along
+ * K, E8M0 scale X = 2^(floor(log2 max|v|) - 2) (exponent clamped to
+ * -127..127; a zero block takes 2^-127) and E2M1 elements nearest to v / X,
+ * ties to the even code, saturating at 6, sign kept (the weights' own
+ * format, with the OCP MX conversion rule).  Both operands then go to the
+ * gfx950 block-scaled FP4 MFMA.  Needs MOE_SCALE_E8M0_G32; runs the sorted
+ * batched kernels for every T (not with FORCE_DECODE or SERIAL).  The
+ * results are the oracle's W4A4 layer, not the W4A16 one. */
+#define MOE_FLAG_W4A4 (1u << 5)
 
 typedef struct moe_w4a16_cfg {
   int32_t abi_version;         /* MOE_W4A16_ABI_VERSION */

@@ -101,7 +101,7 @@ int check_shape(const moe_w4a16_cfg* c) {
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "hidden %d / inter %d not supported", c->hidden,
                 c->inter);
   const uint32_t known = MOE_FLAG_PRENORM | MOE_FLAG_FORCE_DECODE | MOE_FLAG_FORCE_BATCHED |
-                         MOE_FLAG_CHECK_IDS | MOE_FLAG_SERIAL;
+                         MOE_FLAG_CHECK_IDS | MOE_FLAG_SERIAL | MOE_FLAG_W4A4;
   if (c->flags & ~known) return fail(MOE_ERR_INVALID_ARG, "unknown flag bits 0x%x", c->flags);
   if ((c->flags & MOE_FLAG_FORCE_DECODE) && (c->flags & MOE_FLAG_FORCE_BATCHED))
     return fail(MOE_ERR_INVALID_ARG, "FORCE_DECODE and FORCE_BATCHED together");
@@ -109,6 +109,10 @@ int check_shape(const moe_w4a16_cfg* c) {
       (c->num_tokens > 1 || (c->flags & MOE_FLAG_FORCE_BATCHED) ||
        !decode_supported(c->hidden, c->inter)))
     return fail(MOE_ERR_INVALID_ARG, "MOE_FLAG_SERIAL needs T <= 1 on the decode path");
+  if ((c->flags & MOE_FLAG_W4A4) && (c->flags & (MOE_FLAG_FORCE_DECODE | MOE_FLAG_SERIAL)))
+    return fail(MOE_ERR_INVALID_ARG, "MOE_FLAG_W4A4 runs the batched kernels only");
+  if ((c->flags & MOE_FLAG_W4A4) && c->scale_fmt != MOE_SCALE_E8M0_G32)
+    return fail(MOE_ERR_INVALID_ARG, "MOE_FLAG_W4A4 needs E8M0 block scales");
   if ((c->flags & MOE_FLAG_FORCE_DECODE) && !decode_supported(c->hidden, c->inter))
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "no decode kernel for hidden %d / inter %d",
                 c->hidden, c->inter);
@@ -122,7 +126,7 @@ int check_shape(const moe_w4a16_cfg* c) {
 }
 
 bool use_decode(const moe_w4a16_cfg* c) {
-  if (c->flags & MOE_FLAG_FORCE_BATCHED) return false;
+  if (c->flags & (MOE_FLAG_FORCE_BATCHED | MOE_FLAG_W4A4)) return false;
   if (c->flags & MOE_FLAG_FORCE_DECODE) return true;
   return c->num_tokens == 1 && decode_supported(c->hidden, c->inter);
 }

@@ -182,6 +182,91 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// W4A4 ("primitive-ai/LFM2.5-24B-A2B-NVFP4A16", "Why this quant": FP4
+// activations on FP4 matrix hardware).  One K step is two block-scaled FP4
+// MFMAs per matrix (16 x 16 x 128): lane (n, g) gives bytes [32g, 32g + 32)
+// of its weight row's 128-byte step, half h = 16 bytes = one scale block, and
+// the token row's packed codes at the same bytes with the same block's
+// scale, so A and B pair on identical K and identical blocks.  The FP32
+// result of each MFMA is exact at these magnitudes and is added to FP64.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+template <int NMAT>
+__device__ __forceinline__ void wstep_mfma4(const WStep<MOE_SCALE_E8M0_G32, NMAT>& st,
+                                            const uint8_t* arow, const uint8_t* asc,
+                                            double (&acc)[2][4]) {
+  const uint32_t sa = *(const uint16_t*)asc;  // E8M0 of the lane's two token-row blocks
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint4 a = *(const uint4*)(arow + 16 * h);
+    const i32x8 A = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+#pragma unroll
+    for (int mt = 0; mt < NMAT; ++mt) {
+      const uint4 b = st.w[mt][h];
+      const i32x8 B = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+      const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          A, B, f32x4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, (int)((sa >> (8 * h)) & 255u), 0,
+          (int)((st.s[mt] >> (8 * h)) & 255u));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[mt][i] += (double)part[i];
+    }
+  }
+}
+
+// MXFP4 quantisation of the staged token rows, in place (W4A4).  Per block of
+// 32 values: E8M0 code c = max(E - 2, 0) with E the BF16 exponent field of
+// the block's largest magnitude (so X = 2^(c - 127) = 2^(floor(log2 amax) -
+// 2), clamped at 2^-127; a zero block gets 0), then each element's code is the
+// number of E2M1 rounding thresholds its magnitude r = |v| / X passes: the
+// midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5, counted inclusively where
+// the tie goes up to the even code (0.75, 1.75, 3.5) and exclusively where it
+// stays on the even code below; past 5 everything is 6.  The sign bit is
+// copied.  Row r becomes its Kd / 2 packed code bytes followed by Kd / 32
+// scale bytes.  One wave owns a row and reads all of it before writing.
+__device__ __forceinline__ void quant_rows_mxfp4(uint16_t* xs, int ldx, int Kd, int mcnt, int wave,
+                                                 int lane) {
+  const int nblk = Kd / 32;  // at most 128
+  for (int r = wave; r < mcnt; r += kBW) {
+    uint8_t* row = (uint8_t*)(xs + r * ldx);
+    uint4 v[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        v[i][q] = lane + 64 * i < nblk ? *(const uint4*)(row + 64 * (lane + 64 * i) + 16 * q)
+                                       : make_uint4(0u, 0u, 0u, 0u);
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4));  // lgkmcnt(0): the row is read
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int b = lane + 64 * i;
+      if (b >= nblk) continue;
+      const uint32_t w[16] = {v[i][0].x, v[i][0].y, v[i][0].z, v[i][0].w, v[i][1].x, v[i][1].y,
+                              v[i][1].z, v[i][1].w, v[i][2].x, v[i][2].y, v[i][2].z, v[i][2].w,
+                              v[i][3].x, v[i][3].y, v[i][3].z, v[i][3].w};
+      uint32_t amax = 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) amax = max(amax, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+      const uint32_t ex = amax >> 7;
+      const uint32_t sc = ex > 2u ? ex - 2u : 0u;
+      const float inv = __uint_as_float((254u - sc) << 23);  // 2^(127 - sc) = 1 / X
+      uint32_t packed[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const uint32_t bits = (k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xFFFFu);
+        const float m = __uint_as_float((bits & 0x7FFFu) << 16) * inv;
+        uint32_t c = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
+                     (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) +
+                     (uint32_t)(m > 5.0f);
+        c |= (bits >> 12) & 8u;
+        packed[k >> 3] |= c << (4 * (k & 7));
+      }
+      *(uint4*)(row + 16 * b) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+      row[Kd / 2 + b] = (uint8_t)sc;
+    }
+  }
+}
+
 // Stable scan of the routing ids for expert e: the pairs p = t*K + j with
 // ids[p] == e, in increasing p, whose rank lies in [r0, r0 + kMC), go to
 // list[rank - r0].  All threads of the workgroup call it; id0 is the id of
@@ -268,8 +353,9 @@ __device__ __forceinline__ int expert_of(const int* pre, int E, int it) {
   return lo;
 }
 
-template <int FMT, int MODE, int KS>
+template <int FMT, int MODE, int KS, bool A4>
 __global__ __launch_bounds__(64 * kBW, 2) void k_bat_gemm(BatchedArgs a) {
+  static_assert(!A4 || FMT == MOE_SCALE_E8M0_G32, "W4A4 pairs E8M0 scales on both operands");
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   constexpr int NMAT = MODE == 0 ? 2 : 1;
   constexpr int G = FMT == MOE_SCALE_E4M3_G16 ? 16 : 32;
@@ -421,6 +507,10 @@ __global__ __launch_bounds__(64 * kBW, 2) void k_bat_gemm(BatchedArgs a) {
       }
       if (prenorm) lds_barrier();
     }
+    if constexpr (A4) {
+      quant_rows_mxfp4(xs, ldx, Kd, it.mcnt, wave, lane);
+      lds_barrier();
+    }
   };
   double acc[2][4];
 #pragma unroll
@@ -429,9 +519,19 @@ __global__ __launch_bounds__(64 * kBW, 2) void k_bat_gemm(BatchedArgs a) {
     for (int i = 0; i < 4; ++i) acc[mt][i] = 0.0;
   auto compute = [&](const WStep<FMT, NMAT>(&W)[KS], int g) {
     const int tile = g / nst, st = g - tile * nst;
-    const uint16_t* arow = xs + ln * ldx + 64 * gl + st * KS * kKS;
+    if constexpr (A4) {
+      const uint8_t* rb = (const uint8_t*)(xs + ln * ldx);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) wstep_mfma<FMT, NMAT>(W[ks], arow + ks * kKS, acc);
+      for (int ks = 0; ks < KS; ++ks) {
+        const int kg = st * KS + ks;
+        wstep_mfma4<NMAT>(W[ks], rb + kg * (kKS / 2) + 32 * gl, rb + Kd / 2 + kg * (kKS / 32) + 2 * gl,
+                          acc);
+      }
+    } else {
+      const uint16_t* arow = xs + ln * ldx + 64 * gl + st * KS * kKS;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) wstep_mfma<FMT, NMAT>(W[ks], arow + ks * kKS, acc);
+    }
     if (st != nst - 1) return;
     // epilogue: lane holds D[m = 4 gl + i][n] of the M tile
     const int n = (tile % ntiles) * kBN + wave * 16 + ln;
@@ -572,7 +672,7 @@ int cu_count() {
   return n;
 }
 
-template <int FMT, int MODE, int KS>
+template <int FMT, int MODE, int KS, bool A4>
 hipError_t launch_gemm_ks(const BatchedArgs& a, hipStream_t s) {
   const int Kd = MODE == 0 ? a.H : a.I;
   const size_t lds = (size_t)kMC * (Kd + 8) * 2 + (size_t)(kMC + 2 * a.E + 1 + kBW) * 4 + 8 +
@@ -580,18 +680,18 @@ hipError_t launch_gemm_ks(const BatchedArgs& a, hipStream_t s) {
   // The largest shape a check admits (K 4096, 1024 experts) needs 156.3 KiB.
   static size_t allowed = 0;  // benign race: the value only grows towards the same bound
   if (lds > allowed) {
-    hipError_t e = allow_lds(k_bat_gemm<FMT, MODE, KS>, lds);
+    hipError_t e = allow_lds(k_bat_gemm<FMT, MODE, KS, A4>, lds);
     if (e != hipSuccess) return e;
     allowed = lds;
   }
   return launch_kernel(MODE == 0 ? MOE_KERNEL_BATCHED_GATE_UP : MOE_KERNEL_BATCHED_DOWN,
-                       k_bat_gemm<FMT, MODE, KS>, dim3(2 * cu_count()), dim3(64 * kBW), lds, s, a);
+                       k_bat_gemm<FMT, MODE, KS, A4>, dim3(2 * cu_count()), dim3(64 * kBW), lds, s, a);
 }
 
 // K steps per pipeline stage: the largest divisor of the step count up to 2
 // (gate and up: two matrices) or 8 (down), so that two stages of weights fit
 // in registers next to each other without spilling.
-template <int FMT, int MODE>
+template <int FMT, int MODE, bool A4>
 hipError_t launch_gemm(const BatchedArgs& a, hipStream_t s) {
   const int nks = (MODE == 0 ? a.H : a.I) / kKS;
   const int cap = MODE == 0 ? 2 : 8;
@@ -602,22 +702,22 @@ hipError_t launch_gemm(const BatchedArgs& a, hipStream_t s) {
       break;
     }
   switch (ks) {
-    case 8: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 2 : 8)>(a, s);
-    case 7: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 1 : 7)>(a, s);
-    case 6: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 2 : 6)>(a, s);
-    case 5: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 1 : 5)>(a, s);
-    case 4: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 2 : 4)>(a, s);
-    case 3: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 1 : 3)>(a, s);
-    case 2: return launch_gemm_ks<FMT, MODE, 2>(a, s);
-    default: return launch_gemm_ks<FMT, MODE, 1>(a, s);
+    case 8: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 2 : 8), A4>(a, s);
+    case 7: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 1 : 7), A4>(a, s);
+    case 6: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 2 : 6), A4>(a, s);
+    case 5: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 1 : 5), A4>(a, s);
+    case 4: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 2 : 4), A4>(a, s);
+    case 3: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 1 : 3), A4>(a, s);
+    case 2: return launch_gemm_ks<FMT, MODE, 2, A4>(a, s);
+    default: return launch_gemm_ks<FMT, MODE, 1, A4>(a, s);
   }
 }
 
-template <int FMT>
+template <int FMT, bool A4>
 hipError_t launch_batched_fmt(const BatchedArgs& a, hipStream_t s) {
-  hipError_t err = launch_gemm<FMT, 0>(a, s);
+  hipError_t err = launch_gemm<FMT, 0, A4>(a, s);
   if (err != hipSuccess) return err;
-  if ((err = launch_gemm<FMT, 1>(a, s)) != hipSuccess) return err;
+  if ((err = launch_gemm<FMT, 1, A4>(a, s)) != hipSuccess) return err;
   return launch_combine(a.ybuf, a.rw, a.residual, a.out, a.T, a.K, a.H, s);
 }
 
@@ -644,8 +744,11 @@ hipError_t launch_combine(const uint16_t* y, const uint16_t* rw, const uint16_t*
 
 hipError_t launch_batched(const BatchedArgs& a, int fmt, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  return fmt == MOE_SCALE_E4M3_G16 ? launch_batched_fmt<MOE_SCALE_E4M3_G16>(a, s)
-                                   : launch_batched_fmt<MOE_SCALE_E8M0_G32>(a, s);
+  if (a.flags & MOE_FLAG_W4A4)  // the API admits it with E8M0 scales only
+    return fmt == MOE_SCALE_E8M0_G32 ? launch_batched_fmt<MOE_SCALE_E8M0_G32, true>(a, s)
+                                     : hipErrorInvalidValue;
+  return fmt == MOE_SCALE_E4M3_G16 ? launch_batched_fmt<MOE_SCALE_E4M3_G16, false>(a, s)
+                                   : launch_batched_fmt<MOE_SCALE_E8M0_G32, false>(a, s);
 }
 
 }  // namespace moe

@@ -33,6 +33,7 @@ FLAG_FORCE_DECODE = 1 << 1
 FLAG_FORCE_BATCHED = 1 << 2
 FLAG_CHECK_IDS = 1 << 3
 FLAG_SERIAL = 1 << 4
+FLAG_W4A4 = 1 << 5
 
 EXPORTS = [
     "moe_w4a16_abi_version", "moe_w4a16_last_error", "moe_w4a16_shape_supported",

@@ -91,12 +91,12 @@ class Layer:
     def host_tscales(self):
         return S.tensor_scales(self.shape, self.fmt, self.gen_layer)
 
-    def oracle(self, x, ids, rw, residual=None, prenorm=False, eps=EPS, dumps=False):
+    def oracle(self, x, ids, rw, residual=None, prenorm=False, eps=EPS, dumps=False, w4a4=False):
         nib, sc = self.host_tables(ids)
         return O.moe_forward(x, ids, rw, nib, sc, hidden=self.shape.hidden, inter=self.shape.inter,
                              num_experts=self.shape.experts, fmt=self.fmt,
                              tensor_scales=self.host_tscales(), residual=residual,
-                             prenorm=prenorm, eps=eps, dumps=dumps)
+                             prenorm=prenorm, eps=eps, dumps=dumps, w4a4=w4a4)
 
     def gpu(self, x, ids, rw, residual=None, flags=0, eps=EPS, dumps=False, wtab=None):
         sh = self.shape

@@ -32,6 +32,8 @@ def test_constants_match_header():
     assert int(defs["MOE_ERR_WORKSPACE_TOO_SMALL"]) == M.ERR_WORKSPACE_TOO_SMALL
     assert int(defs["MOE_ERR_DEVICE_CHECK"]) == M.ERR_DEVICE_CHECK
     assert int(defs["MOE_SCALE_E4M3_G16"]) == M.SCALE_E4M3_G16
+    for n in ["PRENORM", "FORCE_DECODE", "FORCE_BATCHED", "CHECK_IDS", "SERIAL", "W4A4"]:
+        assert eval(defs["MOE_FLAG_" + n].replace("u", "")) == getattr(M, "FLAG_" + n), n
 
 
 def test_shape_support():
@@ -78,6 +80,9 @@ def cfg(**kw):
     (dict(workspace=FAKE + 8), M.ERR_MISALIGNED),
     (dict(workspace_bytes=100), M.ERR_WORKSPACE_TOO_SMALL),
     (dict(flags=M.FLAG_PRENORM, prenorm_eps=-1.0), M.ERR_INVALID_ARG),
+    (dict(flags=M.FLAG_W4A4, scale_fmt=M.SCALE_E4M3_G16, tensor_scales=FAKE), M.ERR_INVALID_ARG),
+    (dict(flags=M.FLAG_W4A4 | M.FLAG_FORCE_DECODE), M.ERR_INVALID_ARG),
+    (dict(flags=M.FLAG_W4A4 | M.FLAG_SERIAL), M.ERR_INVALID_ARG),
 ])
 def test_cfg_errors(over, code):
     with pytest.raises(M.MoeError) as ei:

@@ -1,0 +1,128 @@
+"""GPU parity of the W4A4 layer (MOE_FLAG_W4A4) against the oracle's W4A4 layer.
+
+"primitive-ai/LFM2.5-24B-A2B-NVFP4A16", "Why this quant": the W4A4 builds make
+the expert activations 4-bit as well and run on FP4 matrix hardware.  Here u
+and every h are quantised to MXFP4 in LDS and multiplied on the gfx950
+block-scaled FP4 MFMA.  Quantised codes are integer decisions taken from the
+same BF16 inputs on both sides, so the dumps (g, v, h, y) are expected to be
+bit-identical almost everywhere; the bound is the tolerance of gpu_helpers.
+"""
+import numpy as np
+import pytest
+import torch
+
+from packed_bit_expert_amd import moe as M
+from packed_bit_expert_amd import synth as S
+from packed_bit_expert_amd.residency import ResidentExperts
+from tests import gpu_helpers as GH
+
+pytestmark = pytest.mark.gpu
+
+LFM = S.LFM24B
+SMALL = S.Shape(hidden=512, inter=256, experts=16, top_k=4, layers=1)
+
+
+def banner(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def layer_mx():
+    banner("upload LFM 2048/1536 E8M0 layer 0")
+    return GH.Layer(LFM, S.FMT_E8M0_G32, 0)
+
+
+@pytest.fixture(scope="module")
+def layer_small():
+    banner("upload 512/256 E8M0 layer 0")
+    return GH.Layer(SMALL, S.FMT_E8M0_G32, 0)
+
+
+def _check(lay, x, ids, rw, residual=None, prenorm=False, what="w4a4"):
+    flags = M.FLAG_W4A4 | (M.FLAG_PRENORM if prenorm else 0)
+    ref, d = lay.oracle(x, ids, rw, residual=residual, prenorm=prenorm, dumps=True, w4a4=True)
+    got, gd, st = lay.gpu(x, ids, rw, residual=residual, flags=flags, dumps=True)
+    assert st == 0
+    for k in ["u", "g", "v", "h", "y"]:
+        GH.compare(gd[k], d[k], f"{what} {k}")
+    GH.compare(got, ref, f"{what} out")
+    return got, ref
+
+
+@pytest.mark.parametrize("workload,prenorm,res", [("c0", False, False), ("c2", False, False),
+                                                  ("c3", True, True), ("c2", True, True)])
+def test_w4a4_layer_full_size(layer_mx, workload, prenorm, res):
+    w = S.WORKLOADS[workload]
+    banner(f"W4A4 {workload} T={w.tokens} prenorm={prenorm} residual={res}")
+    x, ids, rw = S.inputs(w, 0, 0)
+    r = S.activations(7, 0, 0, x.shape[0], LFM.hidden) if res else None
+    _check(layer_mx, x, ids, rw, residual=r, prenorm=prenorm, what=f"w4a4 {workload}")
+
+
+@pytest.mark.parametrize("T", [1, 5, 17, 100])
+def test_w4a4_ragged_tokens(layer_mx, T):
+    banner(f"W4A4 ragged T={T} uniform routing")
+    x = S.activations(11, 0, T, T, LFM.hidden)
+    ids, rw = S.routing_uniform(11, 0, T, T, LFM.experts, 4)
+    _check(layer_mx, x, ids, rw, what=f"w4a4 T={T}")
+
+
+def test_w4a4_small_shape_and_one_expert(layer_small):
+    """Another K (512 / 256: 16 and 8 scale blocks per row) and every pair
+    on one expert (several 16-token passes)."""
+    T = 40
+    banner("W4A4 512/256, 40 tokens all on expert 5")
+    x = S.activations(12, 0, 0, T, SMALL.hidden)
+    ids, rw = S.routing_uniform(12, 0, 0, T, SMALL.experts, 4)
+    rng = np.random.default_rng(12)
+    others = np.array([e for e in range(SMALL.experts) if e != 5])
+    ids = np.stack([np.concatenate([[5], rng.permutation(others)[:3]]) for _ in range(T)])
+    ids = ids.astype(np.int32)
+    assert all(len(set(r)) == 4 for r in ids.tolist())
+    _check(layer_small, x, ids, rw, what="w4a4 small")
+
+
+def test_w4a4_zero_tokens():
+    banner("W4A4 T=0")
+    M.moe_w4a16_forward(0, 0, 0, 0, 0, 0, M.make_cfg(0, flags=M.FLAG_W4A4))
+
+
+def test_w4a4_stack_matches_chain_and_oracle():
+    """Four chained layers (pre-norm + residual) with W4A4: the one-call
+    stack equals four single-layer calls bit for bit, and every layer
+    matches the oracle's W4A4 layer on the oracle chain's input."""
+    L, T = 4, 32
+    banner(f"W4A4 stack L={L} T={T}")
+    store = ResidentExperts(LFM, S.FMT_E8M0_G32, L).fill_synthetic()
+    w = S.WORKLOADS["c2"]
+    x = S.activations(w.family, 0, 3, T, LFM.hidden)
+    ids, rw = zip(*[S.routing(w, l, 3, tokens=T) for l in range(L)])
+    ids, rw = np.stack(ids), np.stack(rw)
+    out = torch.empty((T, LFM.hidden), dtype=torch.bfloat16, device=GH.dev())
+    cfg = M.make_cfg(T, flags=M.FLAG_W4A4, prenorm_eps=GH.EPS)
+    ws = torch.zeros(M.moe_w4a16_workspace_bytes(cfg), dtype=torch.uint8, device=GH.dev())
+    cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), ws.numel()
+    M.moe_w4a16_stack_forward(L, GH.bf16_dev(x), GH.i32_dev(ids), GH.bf16_dev(rw), store.wtab,
+                              store.stab, None, out, cfg)
+    torch.cuda.synchronize()
+    stack = GH.bits_host(out)
+    h = GH.bf16_dev(x)
+    for l in range(L):
+        wt, stb, _ = store.layer_tables(l)
+        o = torch.empty_like(h)
+        c = M.make_cfg(T, flags=M.FLAG_PRENORM | M.FLAG_W4A4, residual=h, prenorm_eps=GH.EPS)
+        wsl = torch.zeros(M.moe_w4a16_workspace_bytes(c), dtype=torch.uint8, device=GH.dev())
+        c.workspace, c.workspace_bytes = wsl.data_ptr(), wsl.numel()
+        M.moe_w4a16_forward(h, GH.i32_dev(ids[l]), GH.bf16_dev(rw[l]), wt, stb, o, c)
+        h = o
+    torch.cuda.synchronize()
+    assert np.array_equal(stack, GH.bits_host(h))
+    hx = x
+    for l in range(L):
+        lay = GH.Layer(LFM, S.FMT_E8M0_G32, l, store=store, l=l)
+        nxt = lay.oracle(hx, ids[l], rw[l], residual=hx, prenorm=True, w4a4=True)
+        got, st = lay.gpu(hx, ids[l], rw[l], residual=hx, flags=M.FLAG_PRENORM | M.FLAG_W4A4)
+        assert st == 0
+        GH.compare(got, nxt, f"w4a4 stack layer{l}")
+        hx = nxt
+    del store
