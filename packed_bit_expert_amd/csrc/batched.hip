@@ -169,19 +169,6 @@ __device__ __forceinline__ void wstep_mfma(const WStep<FMT, NMAT>& st, const uin
   }
 }
 
-// Workgroup barrier for LDS data only.  __syncthreads() (and even an LDS-only
-// fence, because of the direct global->LDS loads) makes every wave wait for
-// all of its loads in flight, the weights included, at each barrier.  Here
-// each wave has already waited for its own direct loads (wait_vm below); the
-// barrier adds the wait for its LDS stores, and the empty asm statements keep
-// the compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4));  // lgkmcnt(0) only
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // W4A4 ("primitive-ai/LFM2.5-24B-A2B-NVFP4A16", "Why this quant": FP4
 // activations on FP4 matrix hardware).  One K step is two block-scaled FP4
 // MFMAs per matrix (16 x 16 x 128): lane (n, g) gives bytes [32g, 32g + 32)
@@ -290,13 +277,6 @@ __device__ void collect_pairs(const int32_t* ids, int id0, int npairs, int e, in
     for (int w = 0; w < kBW; ++w) total += wcnt[w];
     lds_barrier();
   }
-}
-
-// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // Stage the 16 A rows of a pass into LDS with the gfx950 direct global->LDS

@@ -173,10 +173,29 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
   const int sjc = live ? sj : a.T * a.K - 1;
   const int t = sjc / a.K, j = sjc - t * a.K;
 
-  const SlotRef sr = a.pre ? load_slot(a.pre + sjc)
-                           : resolve_slot(a.ids, a.wtab, a.stab, a.tsc, sjc, a.E, a.flags,
-                                          (nb == 0 && lane == 0 && live) ? a.err : nullptr);
-  if (!a.pre && nb == 0 && lane == 0 && live) a.slots[sj] = sr;
+  // 0. the slot's expert (one 32-byte load of the pre-resolved table; without
+  // one the load reads the workspace table, a harmless valid address, and
+  // the slot is resolved below), then the activations, so that both are in
+  // flight together
+  SlotRef sr = load_slot(a.pre ? a.pre + sjc : a.slots);
+  __builtin_amdgcn_sched_barrier(0);
+  const uint16_t* xt = a.x + (size_t)t * H;
+  bf16x2 xp[CPL][16];
+  constexpr int XPT = PRENORM ? (H / 8 + 255) / 256 : 1;  // 16-byte pieces of x per thread
+  uint4 xraw[XPT];
+  if constexpr (PRENORM) {
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const int k8 = threadIdx.x + 256 * u;
+      xraw[u] = k8 < H / 8 ? ldg16(xt + 8 * k8) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (!a.pre) {
+    sr = resolve_slot(a.ids, a.wtab, a.stab, a.tsc, sjc, a.E, a.flags,
+                      (nb == 0 && lane == 0 && live) ? a.err : nullptr);
+    if (nb == 0 && lane == 0 && live) a.slots[sj] = sr;
+  }
   const bool ok = __builtin_amdgcn_readfirstlane(sr.ok) != 0;
   const uint8_t* wbase = ok ? sr.w : (const uint8_t*)a.slots;
   const uint8_t* sbase = ok ? sr.s : (const uint8_t*)a.slots;
@@ -188,17 +207,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
   // 1. loads: activations first (vmcnt retires loads in issue order, so the
   // pre-norm or the first chunk can start while the weights stream), then
   // scale bytes, then weights
-  const uint16_t* xt = a.x + (size_t)t * H;
-  bf16x2 xp[CPL][16];
-  constexpr int XPT = PRENORM ? (H / 8 + 255) / 256 : 1;  // 16-byte pieces of x per thread
-  uint4 xraw[XPT];
-  if constexpr (PRENORM) {
-#pragma unroll
-    for (int u = 0; u < XPT; ++u) {
-      const int k8 = threadIdx.x + 256 * u;
-      xraw[u] = k8 < H / 8 ? ldg16(xt + 8 * k8) : make_uint4(0u, 0u, 0u, 0u);
-    }
-  } else {
+  if constexpr (!PRENORM) {
 #pragma unroll
     for (int i = 0; i < CPL; ++i) unpack16(xt + 32 * (li + LPR * i), xp[i]);
   }
@@ -282,14 +291,18 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
 }
 
 // Grouped down GEMV for ROWS output rows of every slot (one wave per slot),
-// then the slot-order BF16 combine (+ residual) of those rows.
+// then the slot-order BF16 combine (+ residual) of those rows.  The token's h
+// (all k slots, k * I BF16) is read once per workgroup into LDS; every lane
+// then takes its slices from there instead of re-reading them from L2.
 template <int H, int I, int FMT, bool DUMP>
 __global__ __launch_bounds__(256) void k_dec_down(DecodeArgs a) {
   using D = DnShape<I>;
   using M = typename D::M;
   constexpr int LPR = M::LPR, CPL = M::CPL, RPS = M::RPS, NS = D::NS, ROWS = D::ROWS;
   constexpr int G = group_of<FMT>();
+  constexpr int HPT = (I + 255) / 256;  // 16-byte pieces of h per thread for k <= 8
   __shared__ uint16_t ys[8][ROWS];
+  __shared__ __attribute__((aligned(16))) uint16_t hs[8 * I];
 
   const int nblk = H / ROWS;
   const int mb = blockIdx.x % nblk, t = blockIdx.x / nblk;
@@ -297,27 +310,32 @@ __global__ __launch_bounds__(256) void k_dec_down(DecodeArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane % LPR, q = lane / LPR;
   const SlotRef* slots = a.pre ? a.pre : a.slots;
-  // the combine's operands are fetched now, not after the reduction
-  uint16_t rwv[8], resv = 0;
-  if (tid < ROWS) {
-    for (int j = 0; j < a.K; ++j) rwv[j] = a.rw[t * a.K + j];
-    if (a.residual) resv = a.residual[(size_t)t * H + m0 + tid];
-  }
 
-  for (int j = wave; j < a.K; j += 4) {
-    const SlotRef sr = load_slot(slots + t * a.K + j);
+  // 1. loads, in this order: the wave's first slot (its weights depend on
+  // it), the combine's operands, the token's h, then the slot's scales and
+  // weights.  Everything is unconditional with clamped indices, so the loads
+  // go out back to back and each value is waited for only where it is used.
+  // A wave without a slot (k < 4) works on the last one and discards it.
+  const int j0 = min(wave, a.K - 1);
+  const SlotRef sr0 = load_slot(slots + t * a.K + j0);
+  uint16_t rwv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) rwv[j] = a.rw[t * a.K + min(j, a.K - 1)];
+  // (without a residual the load reads a harmless valid address, unused)
+  const uint16_t resv = *(a.residual ? a.residual + (size_t)t * H + m0 + tid % ROWS : a.rw);
+  const int npc = a.K * I / 8;
+  const uint16_t* ht = a.hbuf + (size_t)t * a.K * I;
+  uint4 hv[HPT];
+#pragma unroll
+  for (int u = 0; u < HPT; ++u) hv[u] = ldg16(ht + 8 * min(tid + 256 * u, npc - 1));
+
+  // scales and weights of slot j (a rejected slot reads a harmless valid
+  // address, the slot table)
+  auto issue = [&](const SlotRef& sr, uint4 (&wv)[NS][CPL], uint32_t (&sv)[NS][CPL]) {
     const bool ok = __builtin_amdgcn_readfirstlane(sr.ok) != 0;
-    // a rejected slot reads a harmless valid address (the slot table)
-    const uint8_t* wd = ok ? sr.w + (size_t)I * H : (const uint8_t*)slots;   // after gate and up
+    const uint8_t* wd = ok ? sr.w + (size_t)I * H : (const uint8_t*)slots;  // after gate and up
     const uint8_t* sd = ok ? sr.s + 2 * (size_t)I * (H / G) : (const uint8_t*)slots;
     const size_t row_nib = ok ? I / 2 : 0, row_sc = ok ? I / G : 0;
-    // h slices first (vmcnt retires loads in issue order), then scales, weights
-    const uint16_t* hj = a.hbuf + ((size_t)t * a.K + j) * I;
-    bf16x2 hp[CPL][16];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) unpack16(hj + 32 * (li + LPR * i), hp[i]);
-    uint4 wv[NS][CPL];
-    uint32_t sv[NS][CPL];
 #pragma unroll
     for (int st = 0; st < NS; ++st)
 #pragma unroll
@@ -329,8 +347,14 @@ __global__ __launch_bounds__(256) void k_dec_down(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < CPL; ++i)
         wv[st][i] = ldg16(wd + (size_t)(m0 + st * RPS + q) * row_nib + (ok ? 16 * (li + LPR * i) : 0));
-    __builtin_amdgcn_sched_barrier(0);
-
+  };
+  // y rows of slot j into ys (the dot products, one butterfly over LPR lanes)
+  auto finish = [&](int j, const SlotRef& sr, const uint4 (&wv)[NS][CPL],
+                    const uint32_t (&sv)[NS][CPL]) {
+    const bool ok = __builtin_amdgcn_readfirstlane(sr.ok) != 0;
+    bf16x2 hp[CPL][16];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) unpack16_lds(hs + j * I + 32 * (li + LPR * i), hp[i]);
     double p[NS];
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
@@ -347,12 +371,32 @@ __global__ __launch_bounds__(256) void k_dec_down(DecodeArgs a) {
         if (a.dy) a.dy[((size_t)t * a.K + j) * H + m0 + r] = y;
       }
     }
+  };
+
+  uint4 wv[NS][CPL];
+  uint32_t sv[NS][CPL];
+  issue(sr0, wv, sv);
+  __builtin_amdgcn_sched_barrier(0);
+  // 2. h into LDS (its loads are older than the weights, so only they are
+  // waited for here), then the first slot's rows
+#pragma unroll
+  for (int u = 0; u < HPT; ++u)
+    if (tid + 256 * u < npc) *(uint4*)(hs + 8 * (tid + 256 * u)) = hv[u];
+  lds_barrier();
+  if (wave < a.K) finish(wave, sr0, wv, sv);
+  // 3. slots 4..k-1 (k > 4), one more per wave
+  for (int j = wave + 4; j < a.K; j += 4) {
+    const SlotRef sr = load_slot(slots + t * a.K + j);
+    issue(sr, wv, sv);
+    finish(j, sr, wv, sv);
   }
   __syncthreads();
   if (tid < ROWS) {
     const int m = m0 + tid;
     uint16_t acc = 0;  // +0
-    for (int j = 0; j < a.K; ++j) acc = combine_step(acc, rwv[j], ys[j][tid]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < a.K) acc = combine_step(acc, rwv[j], ys[j][tid]);
     if (a.residual) acc = residual_add(resv, acc);
     a.out[(size_t)t * H + m] = acc;
   }
