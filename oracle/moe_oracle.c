@@ -509,3 +509,40 @@ int oracle_threads_available(void)
     return 1;
 #endif
 }
+
+/* ---------------------------------------------------------------------- */
+/* Hybrid mode: the pinned RAM expert cache                               */
+/* ---------------------------------------------------------------------- */
+
+/* [MXFP4 card], "Bounded pinned RAM expert cache" and "Hybrid mode": CPU-backed
+ * experts of a partially resident layer are served from a packed RAM cache of
+ * contiguous expert triplets with LRU eviction under a memory limit; a miss
+ * rebuilds the triplet from the checkpoint.  Only routed CPU experts are
+ * requested.  Reading where the card is silent: one call requests its
+ * distinct CPU-backed experts in the order of their first appearance in the
+ * ids (token-major, slot order); the cache holds `capacity` triplets.
+ * Plain definition: a list ordered by last use; a request for a key in the
+ * list is a hit and moves it to the front, any other request is a miss that
+ * inserts the key at the front and, when the list is longer than capacity,
+ * drops the key at the back.  keys[n] -> hit[n] (1 = hit).  Returns the
+ * number of hits, or -1 on a bad argument. */
+int oracle_lru(const int64_t* keys, int n, int capacity, uint8_t* hit)
+{
+    if (n < 0 || capacity < 1) return -1;
+    int64_t* list = (int64_t*)malloc(sizeof(int64_t) * (size_t)(capacity + 1));
+    if (!list) return -2;
+    int len = 0, hits = 0;
+    for (int i = 0; i < n; ++i) {
+        int pos = -1;
+        for (int j = 0; j < len; ++j)
+            if (list[j] == keys[i]) { pos = j; break; }
+        hit[i] = pos >= 0;
+        if (pos >= 0) ++hits;
+        else pos = len++;                       /* a new entry, at the back for now */
+        for (int j = pos; j > 0; --j) list[j] = list[j - 1];
+        list[0] = keys[i];                      /* most recently used first */
+        if (len > capacity) --len;              /* the least recently used leaves */
+    }
+    free(list);
+    return hits;
+}

@@ -64,6 +64,8 @@ def _declare(L):
     L.oracle_moe_forward_w4a4.argtypes = L.oracle_moe_forward.argtypes
     L.oracle_quant_mxfp4.restype = C.c_int
     L.oracle_quant_mxfp4.argtypes = [P, C.c_int, C.c_int, P, P]
+    L.oracle_lru.restype = C.c_int
+    L.oracle_lru.argtypes = [P, C.c_int, C.c_int, P]
     L.oracle_threads_available.restype = C.c_int
     L.oracle_threads_available.argtypes = []
     L.oracle_route.restype = C.c_int
@@ -165,6 +167,27 @@ def quant_mxfp4(v):
     if lib().oracle_quant_mxfp4(_ptr(v), rows, cols, _ptr(codes), _ptr(scales)) != 0:
         raise ValueError("oracle_quant_mxfp4: cols must be a multiple of 32")
     return codes, scales
+
+
+def lru(keys, capacity: int) -> np.ndarray:
+    """Hit (1) or miss (0) of each request of an LRU cache of `capacity`
+    entries (see oracle_lru)."""
+    k = _c(keys, np.int64)
+    hit = np.zeros(k.size, np.uint8)
+    if lib().oracle_lru(_ptr(k), k.size, int(capacity), _ptr(hit)) < 0:
+        raise ValueError("oracle_lru: capacity must be >= 1")
+    return hit
+
+
+def lru_requests(ids, cpu_backed) -> list:
+    """The cache requests of one call: the distinct CPU-backed experts of
+    ids [T][K] in order of first appearance (token-major, slot order)."""
+    seen, out = set(), []
+    for e in np.asarray(ids).ravel().tolist():
+        if cpu_backed[e] and e not in seen:
+            seen.add(e)
+            out.append(e)
+    return out
 
 
 def threads_available() -> int:
