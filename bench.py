@@ -35,7 +35,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=64)
     p.add_argument("--workload", default="c1",
                    choices=["c1", "c0", "c2", "c2stack", "c3", "c4", "c4b32", "c1serial",
-                            "c1routed", "c2w4a4", "c3w4a4", "c2stackw4a4"])
+                            "c1routed", "c2w4a4", "c3w4a4", "c2stackw4a4", "c1hybrid"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--calib", action="store_true",
@@ -69,6 +69,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "c1hybrid":
+        run_hybrid(args, dev)
+        return
     shape = S.LFM24B
     wname = {"c2stack": "c2", "c1serial": "c1", "c1routed": "c1", "c2w4a4": "c2", "c3w4a4": "c3",
              "c2stackw4a4": "c2"}.get(args.workload, args.workload)
@@ -292,6 +295,130 @@ def main():
     print(json.dumps(res), flush=True)
 
 
+def run_hybrid(args, dev):
+    """c1 with the MXFP4 card's hybrid split ("Hybrid mode"): the first 1,854
+    experts resident (28 full layers and 62 experts of layer 28), the other
+    578 CPU-backed in a pageable checkpoint copy behind a 2 GiB pinned LRU
+    cache (the card's automatic limit, min(2 GiB, RAM / 4)).  Resident layers
+    run as one stack call; each partially resident layer runs through
+    moe_w4a16_hybrid_forward (ids to the host, cache, one H2D copy per routed
+    CPU expert, grouped layer).  Eager launches: the host steps cannot be
+    captured."""
+    import numpy as np
+    import torch
+
+    from packed_bit_expert_amd import moe as M
+    from packed_bit_expert_amd import synth as S
+    from packed_bit_expert_amd.residency import ResidentExperts
+
+    shape, w = S.LFM24B, S.WORKLOADS["c1"]
+    L, E, K, H, T = shape.layers, shape.experts, shape.top_k, shape.hidden, 1
+    n_res = 1854
+    full, part = n_res // E, n_res % E  # 28 full layers, 62 experts of layer 28
+    t0 = time.time()
+    store = ResidentExperts(shape, w.fmt, full + 1, device=dev).fill_synthetic()
+    nib = shape.nibble_bytes()
+    trip = nib + shape.scale_bytes(w.fmt)
+    ckpt = {}
+    for l in range(full, L):
+        for e in range(E):
+            if l == full and e < part:
+                continue
+            ckpt[(l, e)] = np.concatenate([S.expert_nibbles(shape, w.fmt, l, e),
+                                           S.expert_scales(shape, w.fmt, l, e)])
+    print(f"[bench] {n_res} experts resident, {len(ckpt)} CPU-backed ({len(ckpt) * trip / 1e9:.2f} GB "
+          f"checkpoint in pageable RAM) in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    wt = store.wtab.cpu().numpy()
+    st = store.stab.cpu().numpy()
+    tables = {}
+    for l in range(full, L):
+        rw_ = [int(wt[l, e]) if (l == full and e < part) else 0 for e in range(E)]
+        rs_ = [int(st[l, e]) if (l == full and e < part) else 0 for e in range(E)]
+        src = [0 if (l == full and e < part) else ckpt[(l, e)].ctypes.data for e in range(E)]
+        tables[l] = (rw_, rs_, src)
+    cache_bytes = 2 << 30
+    staging = torch.empty((T * K, trip), dtype=torch.uint8, device=dev)
+    hy = M.moe_w4a16_hybrid_create(trip, nib, cache_bytes, T * K, staging, E, T * K)
+
+    nsteps = args.warmup + args.steps
+    xs = torch.stack([torch.from_numpy(S.activations(w.family, 0, s, T, H).view(np.int16))
+                      for s in range(nsteps)]).view(torch.bfloat16).to(dev)
+    routes = [[S.routing(w, l, s) for l in range(L)] for s in range(nsteps)]
+    ids = torch.from_numpy(np.stack([[r[0] for r in rs] for rs in routes])).to(dev)
+    rws = torch.from_numpy(np.stack([[r[1].view(np.int16) for r in rs] for rs in routes])).view(
+        torch.bfloat16).to(dev)
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    cfg = M.make_cfg(T, prenorm_eps=EPS, stream=stream)
+    ws = torch.zeros(M.moe_w4a16_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), ws.numel()
+    hbuf = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    out = torch.empty((nsteps, T, H), dtype=torch.bfloat16, device=dev)
+
+    def step(s):
+        M.moe_w4a16_stack_forward(full, xs[s], ids[s, :full], rws[s, :full], store.wtab[:full],
+                                  store.stab[:full], None, hbuf[0], cfg)
+        h = hbuf[0]
+        for l in range(full, L):
+            dst = out[s] if l == L - 1 else hbuf[(l - full + 1) % 2]
+            c = M.make_cfg(T, flags=M.FLAG_PRENORM, residual=h, prenorm_eps=EPS, stream=stream)
+            c.workspace, c.workspace_bytes = ws.data_ptr(), ws.numel()
+            rw_, rs_, src = tables[l]
+            M.moe_w4a16_hybrid_forward(hy, h, ids[s, l], rws[s, l], rw_, rs_, src, dst, c)
+            h = dst
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    st0 = M.moe_w4a16_hybrid_stats(hy)
+    t_start = time.perf_counter()
+    for s in range(args.warmup, nsteps):
+        step(s)
+    torch.cuda.synchronize()
+    secs = time.perf_counter() - t_start
+    st1 = M.moe_w4a16_hybrid_stats(hy)
+    moved = st1["h2d_bytes"] - st0["h2d_bytes"]
+    hits = st1["hits"] - st0["hits"]
+    reqs = hits + st1["misses"] - st0["misses"]
+
+    # the host link's ceiling: one 256 MiB pinned-to-device copy
+    src_p = torch.empty(256 << 20, dtype=torch.uint8).pin_memory()
+    dst_d = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    dst_d.copy_(src_p, non_blocking=True)
+    torch.cuda.synchronize()
+    tc = time.perf_counter()
+    for _ in range(4):
+        dst_d.copy_(src_p, non_blocking=True)
+    torch.cuda.synchronize()
+    link = 4 * (256 << 20) / (time.perf_counter() - tc) / 1e9
+    achieved = moved / secs / 1e9
+    M.moe_w4a16_hybrid_destroy(hy)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, shape, args.cpu_seconds)
+    res = {
+        "metric": "MoE-layer tokens/s & achieved HBM GB/s (% of peak), 24B-A2B shape, batch 1/32",
+        "value": L * T * args.steps / secs,
+        "unit": "tokens/s per MoE layer",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": secs / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded E2M1 nibbles, E8M0 117..123 scales, x ~ N(0,1) BF16)",
+        "config": {"workload": workload_name("c1hybrid"), "hidden": H, "inter": shape.inter,
+                   "experts": E, "top_k": K, "layers_per_step": L, "tokens_per_step": T,
+                   "resident_experts": n_res, "cpu_backed_experts": len(ckpt),
+                   "pinned_cache_bytes": cache_bytes, "graph_replay": False,
+                   "stack_tokens_per_s": T * args.steps / secs},
+        "roofline": {"bound": "host link", "achieved": achieved, "peak": link, "unit": "GB/s",
+                     "frac": achieved / link, "traffic": None,
+                     "note": "H2D bytes of routed CPU experts per second of whole steps, against a "
+                             "256 MiB pinned H2D copy measured in the same run"},
+        "host_transfers": {"h2d_bytes_per_step": moved / args.steps,
+                           "routed_cpu_experts_per_step": reqs / args.steps,
+                           "pinned_cache_hit_rate": hits / reqs if reqs else None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def kernel_bytes(shape, w, T, distinct, chained):
     """Algorithmic bytes per launch of each kernel kind: the packed weights and
     scales of the distinct selected experts that kernel reads, plus the
@@ -429,6 +556,8 @@ def workload_name(k):
         "c3w4a4": "prefill S=64 chunks through one layer, W4A4 (MXFP4 activations on the "
                   "block-scaled FP4 MFMA)",
         "c2stackw4a4": "concurrency-32 decode through the 38-layer stack, W4A4",
+        "c1hybrid": "38-layer batch-1 decode, hybrid: 1,854 experts resident, 578 CPU-backed behind "
+                    "a 2 GiB pinned LRU cache (one H2D copy per routed CPU expert)",
     }[k]
 
 

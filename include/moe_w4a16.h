@@ -327,6 +327,61 @@ int moe_w4a16_delay(uint32_t microseconds, void* stream);
 int moe_w4a16_timing_begin(int32_t capacity);
 int moe_w4a16_timing_end(float* ms, int32_t* kinds, int32_t capacity);
 
+/*
+ * Hybrid (partially resident) layers ("LFM2.5-24B-A2B -- Packed MXFP4
+ * Inference", "Hybrid mode" and "Bounded pinned RAM expert cache"), for when
+ * HBM cannot hold every expert.  A handle owns a pinned RAM cache of expert
+ * triplets with LRU eviction under a byte limit, a pinned table and id
+ * buffer, and a small device table; the caller owns the device staging
+ * buffer.  A triplet is one contiguous expert: gate, up and down nibbles
+ * (nibble_bytes = 3 * inter * hidden / 2), then their scales, exactly as the
+ * kernels read a resident expert.
+ *
+ * moe_w4a16_hybrid_create: triplet_bytes and nibble_bytes positive multiples
+ *   of 256; cache_bytes / triplet_bytes >= staging_slots triplets of pinned
+ *   memory (the cache's capacity); device_staging: device, 256-byte aligned,
+ *   staging_slots * triplet_bytes bytes, owned by the caller and not touched
+ *   by anything else while the handle is used; max_experts (<= 1024) and
+ *   max_pairs bound E and T * k of later calls.  Allocates with
+ *   hipHostMalloc/hipMalloc; *out receives the handle.
+ *
+ * moe_w4a16_hybrid_forward: one layer, as moe_w4a16_forward (same x, ids,
+ *   route_w, out and cfg, whose stream is used), where expert e is either
+ *   resident -- resident_w[e] and resident_s[e] (host arrays of device
+ *   pointers) give its nibbles and scales -- or CPU-backed: both are NULL and
+ *   host_src[e] is the host address of its triplet in the checkpoint
+ *   (pageable memory that stays valid and unchanged; it is also the cache
+ *   key).  The call (1) copies the ids to the host and synchronises the
+ *   stream, (2) takes the distinct CPU-backed experts of the ids in order of
+ *   first appearance (token-major, slot order; at most staging_slots of
+ *   them), (3) for each, finds its triplet in the pinned cache or copies it
+ *   there from host_src (a miss, evicting the least recently used), and
+ *   enqueues one H2D copy into staging slot r, (4) enqueues the layer's
+ *   composed pointer tables, and (5) runs the grouped layer.  Only routed CPU
+ *   experts move.  The host work makes this call uncapturable; consecutive
+ *   calls on one handle must use one stream.  Errors: MOE_ERR_INVALID_ARG for
+ *   bad tables, ids out of range (checked on the host), too many routed CPU
+ *   experts or a call larger than the handle's bounds; those of
+ *   moe_w4a16_forward otherwise.
+ *
+ * moe_w4a16_hybrid_stats: stats4 = {calls, cache hits, cache misses, bytes
+ *   copied to the GPU}.  moe_w4a16_hybrid_last_requests: the last call's
+ *   routed CPU experts in request order and whether each hit the cache (room
+ *   for `capacity` entries; *count receives the number).
+ */
+typedef struct moe_w4a16_hybrid moe_w4a16_hybrid;
+int moe_w4a16_hybrid_create(int64_t triplet_bytes, int64_t nibble_bytes, int64_t cache_bytes,
+                            int32_t staging_slots, void* device_staging, int32_t max_experts,
+                            int32_t max_pairs, moe_w4a16_hybrid** out);
+int moe_w4a16_hybrid_destroy(moe_w4a16_hybrid* handle);
+int moe_w4a16_hybrid_forward(moe_w4a16_hybrid* handle, const void* x, const int32_t* expert_ids,
+                             const void* route_w, const void* const* resident_w,
+                             const void* const* resident_s, const void* const* host_src, void* out,
+                             const moe_w4a16_cfg* cfg);
+int moe_w4a16_hybrid_stats(const moe_w4a16_hybrid* handle, int64_t* stats4);
+int moe_w4a16_hybrid_last_requests(const moe_w4a16_hybrid* handle, int32_t* experts,
+                                   uint8_t* hits, int32_t capacity, int32_t* count);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,6 +33,16 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+}  // namespace
+
+// The calling thread's last failure, for the library's other C entry points.
+int moe::report(int code, const char* msg) {
+  if (code == MOE_OK) return ok();
+  return fail(code, "%s", msg);
+}
+
+namespace {
+
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -572,7 +582,7 @@ namespace {
 
 void timing_release() {
   Timing& t = g_timing;
-  for (hipEvent_t e : t.ev) hipEventDestroy(e);
+  for (hipEvent_t e : t.ev) (void)hipEventDestroy(e);
   t = Timing();
 }
 

@@ -107,4 +107,8 @@ hipError_t launch_kernel(int kind, void (*kernel)(KArgs...), dim3 grid, dim3 blo
   return hipGetLastError();
 }
 
+// Records a result code and message as the calling thread's last error (what
+// moe_w4a16_last_error returns); returns code.  MOE_OK clears the message.
+int report(int code, const char* msg);
+
 }  // namespace moe

@@ -42,7 +42,8 @@ EXPORTS = [
     "moe_w4a16_combine", "moe_w4a16_sort_pairs", "moe_w4a16_device_status",
     "moe_w4a16_stream_read", "moe_w4a16_delay", "moe_w4a16_timing_begin",
     "moe_w4a16_timing_end", "moe_w4a16_route", "moe_w4a16_forward_routed",
-    "moe_w4a16_stack_forward_routed",
+    "moe_w4a16_stack_forward_routed", "moe_w4a16_hybrid_create", "moe_w4a16_hybrid_destroy",
+    "moe_w4a16_hybrid_forward", "moe_w4a16_hybrid_stats", "moe_w4a16_hybrid_last_requests",
 ]
 
 
@@ -104,6 +105,14 @@ def lib():
                                                          C.POINTER(Cfg)]),
             "moe_w4a16_timing_begin": (C.c_int, [I32]),
             "moe_w4a16_timing_end": (C.c_int, [C.POINTER(C.c_float), C.POINTER(C.c_int32), I32]),
+            "moe_w4a16_hybrid_create": (C.c_int, [C.c_int64, C.c_int64, C.c_int64, I32, P, I32, I32,
+                                                  C.POINTER(P)]),
+            "moe_w4a16_hybrid_destroy": (C.c_int, [P]),
+            "moe_w4a16_hybrid_forward": (C.c_int, [P, P, P, P, P, P, P, P, C.POINTER(Cfg)]),
+            "moe_w4a16_hybrid_stats": (C.c_int, [P, C.POINTER(C.c_int64)]),
+            "moe_w4a16_hybrid_last_requests": (C.c_int, [P, C.POINTER(C.c_int32),
+                                                         C.POINTER(C.c_uint8), I32,
+                                                         C.POINTER(C.c_int32)]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -267,3 +276,51 @@ def moe_w4a16_stack_forward_routed(num_layers, x, router_w, expert_bias, packed_
                                                 _p(expert_bias), _p(packed_weights), _p(scales),
                                                 _p(tensor_scales), _p(out), _p(expert_ids),
                                                 _p(route_w), C.byref(cfg)))
+
+
+# -- hybrid (partially resident) layers ---------------------------------------------
+
+def moe_w4a16_hybrid_create(triplet_bytes, nibble_bytes, cache_bytes, staging_slots,
+                            device_staging, max_experts, max_pairs) -> int:
+    """Returns the opaque handle (an int)."""
+    h = C.c_void_p()
+    _check(lib().moe_w4a16_hybrid_create(int(triplet_bytes), int(nibble_bytes), int(cache_bytes),
+                                         int(staging_slots), _p(device_staging), int(max_experts),
+                                         int(max_pairs), C.byref(h)))
+    return h.value
+
+
+def moe_w4a16_hybrid_destroy(handle):
+    _check(lib().moe_w4a16_hybrid_destroy(handle))
+
+
+def _ptr_array(values):
+    arr = (C.c_void_p * len(values))()
+    for i, v in enumerate(values):
+        arr[i] = v if v else None
+    return arr
+
+
+def moe_w4a16_hybrid_forward(handle, x, expert_ids, route_w, resident_w, resident_s, host_src,
+                             out, cfg: Cfg):
+    """resident_w / resident_s / host_src: sequences of E ints (device or
+    host addresses, 0 for none)."""
+    rw, rs, hs = _ptr_array(resident_w), _ptr_array(resident_s), _ptr_array(host_src)
+    _check(lib().moe_w4a16_hybrid_forward(handle, _p(x), _p(expert_ids), _p(route_w),
+                                          C.cast(rw, C.c_void_p), C.cast(rs, C.c_void_p),
+                                          C.cast(hs, C.c_void_p), _p(out), C.byref(cfg)))
+
+
+def moe_w4a16_hybrid_stats(handle):
+    """{calls, hits, misses, h2d_bytes}"""
+    st = (C.c_int64 * 4)()
+    _check(lib().moe_w4a16_hybrid_stats(handle, st))
+    return {"calls": st[0], "hits": st[1], "misses": st[2], "h2d_bytes": st[3]}
+
+
+def moe_w4a16_hybrid_last_requests(handle, capacity=1024):
+    ex = (C.c_int32 * capacity)()
+    hit = (C.c_uint8 * capacity)()
+    n = C.c_int32()
+    _check(lib().moe_w4a16_hybrid_last_requests(handle, ex, hit, capacity, C.byref(n)))
+    return list(ex[:n.value]), list(hit[:n.value])

@@ -177,3 +177,27 @@ def test_router_zero_tokens_and_bad_shape():
     with pytest.raises(M.MoeError) as e:
         M.moe_w4a16_route(FAKE, FAKE, None, FAKE, FAKE, c3)
     assert e.value.code == M.ERR_WORKSPACE_TOO_SMALL
+
+
+@pytest.mark.parametrize("args,code", [
+    ((1000, 512, 1 << 20, 1, FAKE, 64, 4), M.ERR_INVALID_ARG),        # triplet not a multiple of 256
+    ((4096, 4096, 1 << 20, 1, FAKE, 64, 4), M.ERR_INVALID_ARG),       # nibbles fill the triplet
+    ((4096, 2048, 1 << 20, 0, FAKE, 64, 4), M.ERR_INVALID_ARG),       # no staging slot
+    ((4096, 2048, 1 << 20, 4, 0, 64, 4), M.ERR_INVALID_ARG),          # no staging buffer
+    ((4096, 2048, 1 << 20, 4, FAKE + 16, 64, 4), M.ERR_MISALIGNED),
+    ((4096, 2048, 3 * 4096, 4, FAKE, 64, 4), M.ERR_INVALID_ARG),     # cache smaller than the staging
+    ((4096, 2048, 1 << 20, 4, FAKE, 2000, 4), M.ERR_INVALID_ARG),     # too many experts
+])
+def test_hybrid_create_argument_errors(args, code):
+    """Checked on the host before anything is allocated."""
+    with pytest.raises(M.MoeError) as e:
+        M.moe_w4a16_hybrid_create(*args)
+    assert e.value.code == code
+
+
+def test_hybrid_null_handle_errors():
+    with pytest.raises(M.MoeError):
+        M.moe_w4a16_hybrid_stats(None)
+    with pytest.raises(M.MoeError):
+        M.moe_w4a16_hybrid_last_requests(None)
+    M.moe_w4a16_hybrid_destroy(None)
