@@ -36,14 +36,17 @@ struct RowMap {
   static constexpr int RPS = 64 / LPR;
 };
 
-// gate/up: K = H; NS load sets per wave (8 loads per lane in total); rows of
-// a set alternate gate n, up n, gate n+1, up n+1, ... so the partner matrix of
-// a row sits LPR lanes away.
+// gate/up: K = H; NS load sets per wave (4 weight loads per lane in total:
+// at H = 2048 one set, 2 rows of gate and 2 of up per wave, 3,072 waves per
+// layer -- twice as many waves with half the work each finish sooner after
+// their data lands than 8 loads per lane did); rows of a set alternate gate n,
+// up n, gate n+1, up n+1, ... so the partner matrix of a row sits LPR lanes
+// away.
 template <int H>
 struct GuShape {
   static constexpr int C = H / 32;
   using M = RowMap<C>;
-  static constexpr int NS = 8 / M::CPL > 0 ? 8 / M::CPL : 1;
+  static constexpr int NS = 4 / M::CPL > 0 ? 4 / M::CPL : 1;
   static constexpr int RW = NS * M::RPS / 2;  // n rows (of gate and of up) per wave
   static_assert(NS <= M::LPR && (NS & (NS - 1)) == 0, "load sets per wave");
 };
