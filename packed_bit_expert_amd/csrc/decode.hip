@@ -240,7 +240,6 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
       const int k8 = threadIdx.x + 256 * u;
       if (k8 >= H / 8) break;
       const uint4 v = xraw[u];
-      *(uint4*)(xs + 8 * k8) = v;
       const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -252,7 +251,21 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
     if (lane == 0) red[wave] = ss;
     __syncthreads();
     const double rs = 1.0 / sqrt((red[0] + red[1] + red[2] + red[3]) / (double)H + (double)a.eps);
-    for (int k = threadIdx.x; k < H; k += 256) xs[k] = f64_to_bf16((double)bf2f(xs[k]) * rs);
+    // each thread rescales the pieces it holds in registers and stores them once
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const int k8 = threadIdx.x + 256 * u;
+      if (k8 >= H / 8) break;
+      const uint32_t w4[4] = {xraw[u].x, xraw[u].y, xraw[u].z, xraw[u].w};
+      uint32_t o4[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t lo = f64_to_bf16((double)__uint_as_float(w4[k] << 16) * rs);
+        const uint32_t hi = f64_to_bf16((double)__uint_as_float(w4[k] & 0xFFFF0000u) * rs);
+        o4[k] = lo | (hi << 16);
+      }
+      *(uint4*)(xs + 8 * k8) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+    }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < CPL; ++i) unpack16_lds(xs + 32 * (li + LPR * i), xp[i]);
