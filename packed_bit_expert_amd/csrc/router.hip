@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ x,
   uint4 wv[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) wv[p] = p < npc ? ldg16(row + 8 * (lane + 64 * p)) : make_uint4(0u, 0u, 0u, 0u);
-  if (xpiece) *(uint4*)(us + 8 * tid) = xv;
+  if (!PRENORM && xpiece) *(uint4*)(us + 8 * tid) = xv;
 
   if (PRENORM) {  // FP64, once per workgroup, the same order as the layer's gate/up kernel
     double ss = 0.0;
@@ -124,10 +124,15 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ x,
     if (lane == 0) red[wave] = ss;
     __syncthreads();
     const double rs = 1.0 / sqrt((red[0] + red[1] + red[2] + red[3]) / (double)H + (double)eps);
-    if (xpiece) {
-      uint16_t* u = us + 8 * tid;
+    if (xpiece) {  // rescaled from the registers, stored once
+      uint32_t o4[4];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) u[k] = f64_to_bf16((double)bf2f(u[k]) * rs);
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = f64_to_bf16((double)__uint_as_float(w4[q] << 16) * rs);
+        const uint32_t hi = f64_to_bf16((double)__uint_as_float(w4[q] & 0xFFFF0000u) * rs);
+        o4[q] = lo | (hi << 16);
+      }
+      *(uint4*)(us + 8 * tid) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
     }
   }
   __syncthreads();
