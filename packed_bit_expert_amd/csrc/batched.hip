@@ -110,21 +110,50 @@ constexpr int kMC = 16;       // tokens per LDS pass
 template <int FMT, int NMAT>
 struct WStep {
   uint4 w[NMAT][2];
-  uint32_t s[NMAT];
+  uint32_t s[NMAT];  // this lane's scales of the step (E8M0: filled from StageScales)
 };
 
-// K step ks of this lane's rows.  A rejected expert (ok = false) reads the
-// same 32 + 4 bytes of a harmless valid buffer for every step instead.
+// E8M0 scales of one stage, 8 bytes (one K step of a row) per step, loaded 16
+// bytes at a time: a scale load is as costly to issue as a weight load, so
+// one 16-byte load per two K steps instead of one 2-byte load per step.
+template <int FMT, int NMAT, int KS>
+struct StageScales {
+  uint32_t q[NMAT][FMT == MOE_SCALE_E8M0_G32 ? 2 * KS : 1];
+};
+
+template <int FMT, int NMAT, int KS>
+__device__ __forceinline__ void load_stage_scales(StageScales<FMT, NMAT, KS>& ss,
+                                                  const uint8_t* const (&srow)[2], int st, bool ok) {
+  if constexpr (FMT == MOE_SCALE_E8M0_G32) {
+#pragma unroll
+    for (int mt = 0; mt < NMAT; ++mt) {
+#pragma unroll
+      for (int p = 0; p < KS / 2; ++p) {
+        const uint4 v = ldg16(srow[mt] + (ok ? (st * KS + 2 * p) * (kKS / 32) : 0));
+        ss.q[mt][4 * p] = v.x;
+        ss.q[mt][4 * p + 1] = v.y;
+        ss.q[mt][4 * p + 2] = v.z;
+        ss.q[mt][4 * p + 3] = v.w;
+      }
+      if constexpr (KS % 2) {  // the last step alone: 8 bytes, never past the row
+        const uint2 v = ldg8(srow[mt] + (ok ? (st * KS + KS - 1) * (kKS / 32) : 0));
+        ss.q[mt][2 * KS - 2] = v.x;
+        ss.q[mt][2 * KS - 1] = v.y;
+      }
+    }
+  }
+}
+
+// K step ks of this lane's rows (E4M3 scales with it).  A rejected expert
+// (ok = false) reads the same first bytes of a harmless valid buffer instead.
 template <int FMT, int NMAT>
 __device__ __forceinline__ void load_wstep(WStep<FMT, NMAT>& st, const uint8_t* const (&wrow)[2],
                                            const uint8_t* const (&srow)[2], int ks, int g,
                                            bool ok) {
   const int wo = ok ? ks * (kKS / 2) + 32 * g : 0;
+  if constexpr (FMT == MOE_SCALE_E4M3_G16) {
 #pragma unroll
-  for (int mt = 0; mt < NMAT; ++mt) {
-    if constexpr (FMT == MOE_SCALE_E8M0_G32)
-      st.s[mt] = ldg<uint16_t>(srow[mt] + (ok ? ks * (kKS / 32) + 2 * g : 0));
-    else
+    for (int mt = 0; mt < NMAT; ++mt)
       st.s[mt] = ldg<uint32_t>(srow[mt] + (ok ? ks * (kKS / 16) + 4 * g : 0));
   }
 #pragma unroll
@@ -339,7 +368,8 @@ __global__ __launch_bounds__(64 * kBW, 2) void k_bat_gemm(BatchedArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   constexpr int NMAT = MODE == 0 ? 2 : 1;
   constexpr int G = FMT == MOE_SCALE_E4M3_G16 ? 16 : 32;
-  constexpr int NLOADS = 3 * KS * NMAT;  // vector loads of one stage, per lane
+  // vector loads of one stage, per lane
+  constexpr int NLOADS = FMT == MOE_SCALE_E8M0_G32 ? (2 * KS + (KS + 1) / 2) * NMAT : 3 * KS * NMAT;
   const int Kd = MODE == 0 ? a.H : a.I;
   const int Nd = MODE == 0 ? a.I : a.H;
   const int ntiles = Nd / kBN, nst = Kd / (kKS * KS);
@@ -448,7 +478,7 @@ __global__ __launch_bounds__(64 * kBW, 2) void k_bat_gemm(BatchedArgs a) {
       srow[0] = srow[1] = isc + (iok ? 2 * (size_t)a.I * (a.H / G) + nn * rows : 0);
     }
   };
-  auto issue = [&](WStep<FMT, NMAT>(&W)[KS], int g) {
+  auto issue = [&](WStep<FMT, NMAT>(&W)[KS], StageScales<FMT, NMAT, KS>& SQ, int g) {
     const int tile = g / nst, st = g - tile * nst;
     if (tile / ntiles != iss_item) {
       iss_item = tile / ntiles;
@@ -459,6 +489,7 @@ __global__ __launch_bounds__(64 * kBW, 2) void k_bat_gemm(BatchedArgs a) {
       isc = iok ? ts[e] : (const uint8_t*)a.x;
     }
     rows_for(tile % ntiles);
+    load_stage_scales<FMT, NMAT, KS>(SQ, srow, st, iok);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) load_wstep<FMT, NMAT>(W[ks], wrow, srow, st * KS + ks, gl, iok);
   };
@@ -497,8 +528,16 @@ __global__ __launch_bounds__(64 * kBW, 2) void k_bat_gemm(BatchedArgs a) {
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[mt][i] = 0.0;
-  auto compute = [&](const WStep<FMT, NMAT>(&W)[KS], int g) {
+  auto compute = [&](WStep<FMT, NMAT>(&W)[KS], const StageScales<FMT, NMAT, KS>& SQ, int g) {
     const int tile = g / nst, st = g - tile * nst;
+    if constexpr (FMT == MOE_SCALE_E8M0_G32) {
+      // the lane's two scale bytes of each step: bytes 2 gl, 2 gl + 1 of its 8
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt)
+          W[ks].s[mt] = ((gl >> 1) ? SQ.q[mt][2 * ks + 1] : SQ.q[mt][2 * ks]) >> (16 * (gl & 1)) & 0xFFFFu;
+    }
     if constexpr (A4) {
       const uint8_t* rb = (const uint8_t*)(xs + ln * ldx);
 #pragma unroll
@@ -551,14 +590,15 @@ __global__ __launch_bounds__(64 * kBW, 2) void k_bat_gemm(BatchedArgs a) {
   // finds its pairs and starts its token rows while its first stage is
   // already in flight.
   WStep<FMT, NMAT> W0[KS], W1[KS];
+  StageScales<FMT, NMAT, KS> S0, S1;
   int g = t0 * nst;
   const int gend = t1 * nst;
   auto item_of = [&](int gg) { return gg / nst / ntiles; };
   auto next = [&](int gg) { return gg + 1 < gend ? gg + 1 : gg; };
-  issue(W0, g);
+  issue(W0, S0, g);
   setup_item(item_of(g));
   __builtin_amdgcn_sched_barrier(0);
-  issue(W1, next(g));
+  issue(W1, S1, next(g));
   __builtin_amdgcn_sched_barrier(0);
   wait_vm<NLOADS>();  // the token rows (and stage g) have landed
   rows_ready(g / nst);
@@ -568,7 +608,7 @@ __global__ __launch_bounds__(64 * kBW, 2) void k_bat_gemm(BatchedArgs a) {
   // the next stage is issued: with direct-to-LDS loads possibly in flight the
   // compiler would otherwise wait for all loads before every LDS read.
   for (;;) {
-    compute(W0, g);
+    compute(W0, S0, g);
     if (++g >= gend) break;
     bool change = item_of(g) != item_of(g - 1);
     if (change) {
@@ -577,10 +617,10 @@ __global__ __launch_bounds__(64 * kBW, 2) void k_bat_gemm(BatchedArgs a) {
       wait_vm<0>();  // the token rows (and W1, issued a stage ago) have landed
     }
     __builtin_amdgcn_sched_barrier(0);
-    issue(W0, next(g));
+    issue(W0, S0, next(g));
     __builtin_amdgcn_sched_barrier(0);  // no use of W1 above these loads
     if (change) rows_ready(g / nst);
-    compute(W1, g);
+    compute(W1, S1, g);
     if (++g >= gend) break;
     change = item_of(g) != item_of(g - 1);
     if (change) {
@@ -589,7 +629,7 @@ __global__ __launch_bounds__(64 * kBW, 2) void k_bat_gemm(BatchedArgs a) {
       wait_vm<0>();
     }
     __builtin_amdgcn_sched_barrier(0);
-    issue(W1, next(g));
+    issue(W1, S1, next(g));
     __builtin_amdgcn_sched_barrier(0);
     if (change) rows_ready(g / nst);
   }
