@@ -229,6 +229,24 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     stream_gbps = 5 * buf.numel() / (e0.elapsed_time(e1) / 1e3) / 1e9
+    # the dominant kernel's bytes read by one launch of the plain stream read
+    # (16-byte loads, no arithmetic, no dependent loads), each launch at a new
+    # offset of the 1 GiB buffer so that it reads HBM, not the memory-side
+    # cache: what launch and memory latency alone cost a kernel of this size
+    plain_us = None
+    if dominant is not None and dominant.get("alg_bytes_per_launch"):
+        nb = int(dominant["alg_bytes_per_launch"]) // 4096 * 4096
+        nreg = buf.numel() // nb
+        ts = []
+        for c0 in range(0, 256, 64):
+            M.moe_w4a16_delay(30000, stream)
+            M.moe_w4a16_timing_begin(64)
+            for i in range(c0, c0 + 64):
+                M.moe_w4a16_stream_read(buf.data_ptr() + (i % nreg) * nb, nb, sink, stream)
+            msl, _ = M.moe_w4a16_timing_end(64)
+            ts += msl
+        torch.cuda.synchronize()
+        plain_us = float(np.mean(ts) * 1e3)
     if args.calib:
         # counter calibration: one more 1 GiB read and a 256 MiB device copy
         M.moe_w4a16_stream_read(buf, buf.numel(), sink, stream)
@@ -248,7 +266,9 @@ def main():
                 "traffic": traffic_for(dominant["_kind"], args.workload),
                 "kernel": dominant["kernel"],
                 "alg_bytes_per_launch": dominant["alg_bytes_per_launch"],
-                "mean_launch_us": dominant["mean_us"]}
+                "mean_launch_us": dominant["mean_us"],
+                "plain_read_same_bytes_us": plain_us,
+                "frac_of_plain_read": plain_us / dominant["mean_us"] if plain_us else None}
         if dominant["_kind"] in (4, 5):
             fl = kernel_flops(shape, T, dominant["_kind"])
             roof["mfma_useful_TFLOPs"] = fl / (dominant["mean_us"] / 1e6) / 1e12

@@ -287,9 +287,10 @@ int moe_w4a16_sort_pairs(const int32_t* expert_ids, int32_t num_tokens, int32_t 
 int moe_w4a16_device_status(void* workspace, int32_t* host_code, void* stream);
 
 /* Measurement helper: stream-read `bytes` (multiple of 16) from device
- * memory `src` with 16-byte loads over the whole GPU and write one word per
- * workgroup to `sink` (device, 4 * 4096 bytes), to measure the achievable
- * HBM read bandwidth next to the kernels above. */
+ * memory `src` with 16-byte loads over the whole GPU (256 to 4096
+ * workgroups, sized to the buffer) and write one word per workgroup to
+ * `sink` (device, 4 * 4096 bytes), to measure the achievable HBM read
+ * bandwidth next to the kernels above. */
 int moe_w4a16_stream_read(const void* src, size_t bytes, void* sink, void* stream);
 
 /* Measurement helper: one wave that spins for `microseconds` (at most

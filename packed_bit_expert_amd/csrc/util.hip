@@ -38,6 +38,8 @@ __global__ __launch_bounds__(256) void k_zero(uint8_t* p, size_t bytes) {
   if (blockIdx.x == 0 && threadIdx.x < (bytes & 15)) p[16 * n16 + threadIdx.x] = 0;
 }
 
+// Plain read of n16 16-byte words, grid-strided; the grid is sized to the
+// buffer (launch_stream_read).
 __global__ __launch_bounds__(256) void k_stream_read(const uint4* __restrict__ src, size_t n16,
                                                      uint32_t* __restrict__ sink) {
   __shared__ uint32_t red;
@@ -85,8 +87,11 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
 }
 
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s) {
-  return launch_kernel(MOE_KERNEL_STREAM_READ, k_stream_read, dim3(4096), dim3(256), 0, s,
-                       (const uint4*)src, bytes / 16, sink);
+  // two 16-byte words per thread at least, 256 to 4096 workgroups
+  const size_t n16 = bytes / 16;
+  const unsigned grid = (unsigned)std::min<size_t>(4096, std::max<size_t>(256, (n16 + 511) / 512));
+  return launch_kernel(MOE_KERNEL_STREAM_READ, k_stream_read, dim3(grid), dim3(256), 0, s,
+                       (const uint4*)src, n16, sink);
 }
 
 hipError_t launch_delay(uint32_t microseconds, hipStream_t s) {
