@@ -27,6 +27,17 @@ __device__ void router_select(const double* logits, const float* bias, int E, in
                               int32_t* ids, uint16_t* rw) {
   double s[4], c[4];
   bool taken[4];
+  double l[4];
+  float bv[4];
+  // without a bias, a harmless read of the logits (its value is not used),
+  // so that every load is unconditional and all are in flight together
+  const float* bsrc = bias ? bias : (const float*)logits;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i < E ? lane + 64 * i : 0;
+    l[i] = __hip_atomic_load(logits + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bv[i] = bsrc[e];
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
@@ -34,9 +45,8 @@ __device__ void router_select(const double* logits, const float* bias, int E, in
     s[i] = 0.0;
     c[i] = 0.0;
     if (e < E) {
-      const double l = __hip_atomic_load(logits + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s[i] = 1.0 / (1.0 + exp(-l));
-      c[i] = s[i] + (bias ? (double)bias[e] : 0.0);
+      s[i] = 1.0 / (1.0 + exp(-l[i]));
+      c[i] = s[i] + (bias ? (double)bv[i] : 0.0);
     }
   }
   double my_s = 0.0;  // lane j keeps slot j's score and expert
@@ -87,9 +97,11 @@ __device__ void router_select(const double* logits, const float* bias, int E, in
 // H = 2048) and is pre-normed there once per workgroup in FP64; lane l of a
 // wave holds the router-row pieces l, l + 64, ... (H a multiple of 512, at
 // most 2048: at most 4 pieces), loaded before x is waited for.  The
-// workgroup's logits leave together (one store, one release, one count); the
-// token's last workgroup to finish selects -- an atomic count that nobody
-// waits on.  count[T] starts at 0 and is left at 0.
+// workgroup's logits leave together as device-coherent stores; once they
+// have completed, the workgroup counts itself in, and the token's last
+// workgroup to finish selects, reading the logits with device-coherent loads
+// -- an atomic count that nobody waits on, and no cache write-back or
+// invalidation.  count[T] starts at 0 and is left at 0.
 template <bool PRENORM>
 __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ x,
                                                 const uint16_t* __restrict__ wr,
@@ -158,14 +170,17 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ x,
       if (blockIdx.y * 4 + w < E)
         __hip_atomic_store(logits + (size_t)t * E + blockIdx.y * 4 + w, lgs[w], __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t prev = __hip_atomic_fetch_add(count + t, 1u, __ATOMIC_ACQ_REL,
+    // the logits are device-coherent stores: once they have completed, the
+    // count can be taken without writing back or invalidating any cache
+    __builtin_amdgcn_s_waitcnt(0);
+    const uint32_t prev = __hip_atomic_fetch_add(count + t, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     last = prev == gridDim.y - 1;
     if (last) __hip_atomic_store(count + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (!last || wave != 0) return;
-  __atomic_thread_fence(__ATOMIC_ACQUIRE);
+  // router_select reads the logits with device-coherent loads
   router_select(logits + (size_t)t * E, bias, E, K, lane, ids + (size_t)t * K, rw + (size_t)t * K);
 }
 
