@@ -71,7 +71,7 @@ bool capturing(hipStream_t s) {
 constexpr int kStackGroup = 64;  // layers whose routing slots are resolved in one pass
 
 struct Layout {
-  size_t hbuf, ybuf, ping, scratch, logits, rcount, slots, total;
+  size_t hbuf, ybuf, ping, scratch, ubuf, logits, rcount, slots, total;
 };
 
 Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
@@ -84,6 +84,8 @@ Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
   L.ping = off;
   off += align256((size_t)(T * H) * 2);
   L.scratch = off;  // serial mode: the per-slot launches' unused combine output
+  off += align256((size_t)(T * H) * 2);
+  L.ubuf = off;  // batched: the pre-normed layer input
   off += align256((size_t)(T * H) * 2);
   L.logits = off;  // router logits, FP64 [T][E]
   off += align256((size_t)(T * E) * 8);
@@ -151,6 +153,8 @@ struct Call {
   const void* residual;
   void* out;
   const moe_w4a16_dump* dump;
+  bool x_normed = false;  // batched stack: the workspace's u already holds prenorm(x)
+  bool norm_out = false;  // batched stack: the combine also writes prenorm(out) there
 };
 
 int check_call(const moe_w4a16_cfg* c, const Call& k) {
@@ -271,6 +275,9 @@ int run_layer(const moe_w4a16_cfg* c, const Call& k, const SlotRef* pre = nullpt
   a.dh = d ? (uint16_t*)d->h : nullptr;
   a.dy = d ? (uint16_t*)d->y : nullptr;
   a.err = err;
+  a.ubuf = (uint16_t*)(ws + L.ubuf);
+  a.unext = k.norm_out ? a.ubuf : nullptr;
+  a.x_normed = k.x_normed;
   a.T = T;
   a.H = c->hidden;
   a.I = c->inter;
@@ -371,6 +378,9 @@ int moe_w4a16_stack_forward(int32_t num_layers, const void* x, const int32_t* ex
     Call kl{src, expert_ids + (size_t)l * T * K, (const uint16_t*)route_w + (size_t)l * T * K,
             packed_weights + (size_t)l * E, scales + (size_t)l * E, lc.tensor_scales, src, dst,
             nullptr};
+    // batched: each layer's combine leaves the next layer's pre-normed input
+    kl.x_normed = !decode && l > 0;
+    kl.norm_out = !decode && l + 1 < num_layers;
     rc = run_layer(&lc, kl, decode ? slots + (size_t)g * T * K : nullptr);
     if (rc) return rc;
     src = dst;
@@ -549,6 +559,9 @@ extern "C" int moe_w4a16_stack_forward_routed(int32_t num_layers, const void* x,
     lc.tensor_scales = tensor_scales ? tensor_scales + (size_t)l * E * 2 : nullptr;
     Call kl{src, ids_l, rw_l, packed_weights + (size_t)l * E, scales + (size_t)l * E,
             lc.tensor_scales, src, dst, nullptr};
+    const bool batched = !use_decode(&lc);
+    kl.x_normed = batched && l > 0;
+    kl.norm_out = batched && l + 1 < num_layers;
     rc = run_layer(&lc, kl);
     if (rc) return rc;
     src = dst;

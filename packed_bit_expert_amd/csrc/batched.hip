@@ -493,30 +493,16 @@ __global__ __launch_bounds__(64 * kBW, 2) void k_bat_gemm(BatchedArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) load_wstep<FMT, NMAT>(W[ks], wrow, srow, st * KS + ks, gl, iok);
   };
-  // after the token rows of a new item have landed: pre-norm and dumps
+  // after the token rows of a new item have landed: the dump of u (the
+  // pre-norm, if any, was applied to x before the launch)
   auto rows_ready = [&](int first_tile) {
     lds_barrier();  // every wave's token rows are in LDS
-    if (MODE == 0) {
-      const bool prenorm = (a.flags & MOE_FLAG_PRENORM) != 0;
-      const bool dump = a.du && first_tile % ntiles == 0;
+    if (MODE == 0 && a.du && first_tile % ntiles == 0) {
       for (int r = wave; r < it.mcnt; r += kBW) {
-        uint16_t* row = xs + r * ldx;
-        if (prenorm) {
-          double ss = 0.0;
-          for (int k = lane; k < Kd; k += 64) {
-            const double f = bf2f(row[k]);
-            ss += f * f;
-          }
-          ss = seg_finish<32, double>(ss, lane);
-          const double rs = 1.0 / sqrt(ss / (double)Kd + (double)a.eps);
-          for (int k = lane; k < Kd; k += 64) row[k] = f64_to_bf16((double)bf2f(row[k]) * rs);
-        }
-        if (dump) {
-          const int t = list[r] / a.K;
-          for (int k = lane; k < Kd; k += 64) a.du[(size_t)t * Kd + k] = row[k];
-        }
+        const uint16_t* row = xs + r * ldx;
+        const int t = list[r] / a.K;
+        for (int k = lane; k < Kd; k += 64) a.du[(size_t)t * Kd + k] = row[k];
       }
-      if (prenorm) lds_barrier();
     }
     if constexpr (A4) {
       quant_rows_mxfp4(xs, ldx, Kd, it.mcnt, wave, lane);
@@ -636,41 +622,109 @@ __global__ __launch_bounds__(64 * kBW, 2) void k_bat_gemm(BatchedArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 4. slot-order combine: 8 consecutive outputs per thread
+// 4. slot-order combine: 8 consecutive outputs per thread.  With NORM (one
+// workgroup per token, H <= 2048) the workgroup also writes u = the
+// weightless RMS pre-norm of its output row, the next layer's input.
 // ---------------------------------------------------------------------------
+// Sum of squares of a row's BF16 values in FP64 over the workgroup (exact:
+// every square fits FP64 and so does their sum at these magnitudes), then
+// the row's scale 1 / sqrt(mean + eps).
+__device__ __forceinline__ double row_rscale(double ss, int H, float eps, double* red) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  ss = seg_finish<32, double>(ss, lane);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  return 1.0 / sqrt((red[0] + red[1] + red[2] + red[3]) / (double)H + (double)eps);
+}
+
+__device__ __forceinline__ double sq8(uint4 v) {
+  const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+  double ss = 0.0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const double lo = __uint_as_float(w4[q] << 16), hi = __uint_as_float(w4[q] & 0xFFFF0000u);
+    ss += lo * lo + hi * hi;
+  }
+  return ss;
+}
+
+__device__ __forceinline__ uint4 scale8(uint4 v, double rs) {
+  const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o4[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t lo = f64_to_bf16((double)__uint_as_float(w4[q] << 16) * rs);
+    const uint32_t hi = f64_to_bf16((double)__uint_as_float(w4[q] & 0xFFFF0000u) * rs);
+    o4[q] = lo | (hi << 16);
+  }
+  return make_uint4(o4[0], o4[1], o4[2], o4[3]);
+}
+
+template <bool NORM>
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
                                                  const uint16_t* __restrict__ rw,
                                                  const uint16_t* __restrict__ residual,
-                                                 uint16_t* __restrict__ out, int K, int H) {
+                                                 uint16_t* __restrict__ out, int K, int H,
+                                                 uint16_t* __restrict__ u, float eps) {
+  __shared__ double red[4];
   const int t = blockIdx.y;
   const int m8 = blockIdx.x * 256 + threadIdx.x;
-  if (8 * m8 >= H) return;
-  uint16_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int j = 0; j < K; ++j) {
-    const uint16_t w = rw[t * K + j];
-    const uint4 v = *(const uint4*)(y + ((size_t)t * K + j) * H + 8 * m8);
-    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+  const bool live = 8 * m8 < H;
+  if (!NORM && !live) return;
+  uint4 o = make_uint4(0u, 0u, 0u, 0u);
+  if (live) {
+    uint16_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < K; ++j) {
+      const uint16_t w = rw[t * K + j];
+      const uint4 v = *(const uint4*)(y + ((size_t)t * K + j) * H + 8 * m8);
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] = combine_step(acc[2 * q], w, (uint16_t)(w4[q] & 0xFFFFu));
-      acc[2 * q + 1] = combine_step(acc[2 * q + 1], w, (uint16_t)(w4[q] >> 16));
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = combine_step(acc[2 * q], w, (uint16_t)(w4[q] & 0xFFFFu));
+        acc[2 * q + 1] = combine_step(acc[2 * q + 1], w, (uint16_t)(w4[q] >> 16));
+      }
     }
-  }
-  if (residual) {
-    const uint4 v = *(const uint4*)(residual + (size_t)t * H + 8 * m8);
-    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    if (residual) {
+      const uint4 v = *(const uint4*)(residual + (size_t)t * H + 8 * m8);
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] = residual_add((uint16_t)(w4[q] & 0xFFFFu), acc[2 * q]);
-      acc[2 * q + 1] = residual_add((uint16_t)(w4[q] >> 16), acc[2 * q + 1]);
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = residual_add((uint16_t)(w4[q] & 0xFFFFu), acc[2 * q]);
+        acc[2 * q + 1] = residual_add((uint16_t)(w4[q] >> 16), acc[2 * q + 1]);
+      }
     }
+    o.x = acc[0] | ((uint32_t)acc[1] << 16);
+    o.y = acc[2] | ((uint32_t)acc[3] << 16);
+    o.z = acc[4] | ((uint32_t)acc[5] << 16);
+    o.w = acc[6] | ((uint32_t)acc[7] << 16);
+    *(uint4*)(out + (size_t)t * H + 8 * m8) = o;
   }
-  uint4 o;
-  o.x = acc[0] | ((uint32_t)acc[1] << 16);
-  o.y = acc[2] | ((uint32_t)acc[3] << 16);
-  o.z = acc[4] | ((uint32_t)acc[5] << 16);
-  o.w = acc[6] | ((uint32_t)acc[7] << 16);
-  *(uint4*)(out + (size_t)t * H + 8 * m8) = o;
+  if constexpr (NORM) {
+    const double rs = row_rscale(live ? sq8(o) : 0.0, H, eps, red);
+    if (live) *(uint4*)(u + (size_t)t * H + 8 * m8) = scale8(o, rs);
+  }
+}
+
+// The weightless RMS pre-norm of each row of x: u = bf16(x * rsqrt(mean(x^2)
+// + eps)), FP64; one workgroup per token, H <= 4096.
+__global__ __launch_bounds__(256) void k_prenorm(const uint16_t* __restrict__ x,
+                                                 uint16_t* __restrict__ u, int H, float eps) {
+  __shared__ double red[4];
+  const int t = blockIdx.x;
+  uint4 v[2];
+  double ss = 0.0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int k8 = threadIdx.x + 256 * i;
+    v[i] = k8 < H / 8 ? ldg16(x + (size_t)t * H + 8 * k8) : make_uint4(0u, 0u, 0u, 0u);
+    ss += sq8(v[i]);
+  }
+  const double rs = row_rscale(ss, H, eps, red);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int k8 = threadIdx.x + 256 * i;
+    if (k8 < H / 8) *(uint4*)(u + (size_t)t * H + 8 * k8) = scale8(v[i], rs);
+  }
 }
 
 template <typename KernelT>
@@ -738,7 +792,7 @@ hipError_t launch_batched_fmt(const BatchedArgs& a, hipStream_t s) {
   hipError_t err = launch_gemm<FMT, 0, A4>(a, s);
   if (err != hipSuccess) return err;
   if ((err = launch_gemm<FMT, 1, A4>(a, s)) != hipSuccess) return err;
-  return launch_combine(a.ybuf, a.rw, a.residual, a.out, a.T, a.K, a.H, s);
+  return launch_combine(a.ybuf, a.rw, a.residual, a.out, a.T, a.K, a.H, s, a.unext, a.eps);
 }
 
 }  // namespace
@@ -755,15 +809,37 @@ hipError_t launch_sort(const int32_t* ids, int npairs, int E, int32_t* counts, i
 }
 
 hipError_t launch_combine(const uint16_t* y, const uint16_t* rw, const uint16_t* residual,
-                          uint16_t* out, int T, int K, int H, hipStream_t s) {
+                          uint16_t* out, int T, int K, int H, hipStream_t s, uint16_t* u,
+                          float eps) {
   if (T == 0) return hipSuccess;
   dim3 grid((H / 8 + 255) / 256, T);
-  return launch_kernel(MOE_KERNEL_COMBINE, k_combine, grid, dim3(256), 0, s, y, rw, residual, out,
-                       K, H);
+  if (u && H <= 2048)
+    return launch_kernel(MOE_KERNEL_COMBINE, k_combine<true>, grid, dim3(256), 0, s, y, rw,
+                         residual, out, K, H, u, eps);
+  hipError_t e = launch_kernel(MOE_KERNEL_COMBINE, k_combine<false>, grid, dim3(256), 0, s, y, rw,
+                               residual, out, K, H, (uint16_t*)nullptr, eps);
+  if (e != hipSuccess || !u) return e;
+  return launch_prenorm(out, u, T, H, eps, s);
 }
 
-hipError_t launch_batched(const BatchedArgs& a, int fmt, hipStream_t s) {
-  if (a.T == 0) return hipSuccess;
+hipError_t launch_prenorm(const uint16_t* x, uint16_t* u, int T, int H, float eps, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  return launch_kernel(MOE_KERNEL_PRENORM, k_prenorm, dim3(T), dim3(256), 0, s, x, u, H, eps);
+}
+
+hipError_t launch_batched(const BatchedArgs& a0, int fmt, hipStream_t s) {
+  if (a0.T == 0) return hipSuccess;
+  // the pre-norm once per call (or already done by the previous layer's
+  // combine), not once per workgroup and item inside the GEMM
+  BatchedArgs a = a0;
+  if (a.flags & MOE_FLAG_PRENORM) {
+    if (!a.x_normed) {
+      const hipError_t e = launch_prenorm(a.x, a.ubuf, a.T, a.H, a.eps, s);
+      if (e != hipSuccess) return e;
+    }
+    a.x = a.ubuf;
+    a.flags &= ~MOE_FLAG_PRENORM;
+  }
   if (a.flags & MOE_FLAG_W4A4)  // the API admits it with E8M0 scales only
     return fmt == MOE_SCALE_E8M0_G32 ? launch_batched_fmt<MOE_SCALE_E8M0_G32, true>(a, s)
                                      : hipErrorInvalidValue;
