@@ -106,6 +106,9 @@ __global__ __launch_bounds__(256) void k_sort(const int32_t* __restrict__ ids, i
 constexpr int kBW = 4;        // waves per workgroup
 constexpr int kBN = 16 * kBW; // output rows per workgroup
 constexpr int kMC = 16;       // tokens per LDS pass
+// persistent workgroups per CU (gate/up, down): down's smaller token rows and
+// K-stages let three share a CU, which keeps more of its loads in flight
+constexpr int kWgPerCu[2] = {2, 3};
 
 template <int FMT, int NMAT>
 struct WStep {
@@ -363,7 +366,7 @@ __device__ __forceinline__ int expert_of(const int* pre, int E, int it) {
 }
 
 template <int FMT, int MODE, int KS, bool A4>
-__global__ __launch_bounds__(64 * kBW, 2) void k_bat_gemm(BatchedArgs a) {
+__global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedArgs a) {
   static_assert(!A4 || FMT == MOE_SCALE_E8M0_G32, "W4A4 pairs E8M0 scales on both operands");
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   constexpr int NMAT = MODE == 0 ? 2 : 1;
@@ -758,17 +761,20 @@ hipError_t launch_gemm_ks(const BatchedArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     allowed = lds;
   }
+  // as many workgroups per CU as the occupancy target and the LDS allow
+  int per = kWgPerCu[MODE];
+  while (per > 1 && (size_t)per * lds > 160 * 1024) --per;
   return launch_kernel(MODE == 0 ? MOE_KERNEL_BATCHED_GATE_UP : MOE_KERNEL_BATCHED_DOWN,
-                       k_bat_gemm<FMT, MODE, KS, A4>, dim3(2 * cu_count()), dim3(64 * kBW), lds, s, a);
+                       k_bat_gemm<FMT, MODE, KS, A4>, dim3(per * cu_count()), dim3(64 * kBW), lds, s, a);
 }
 
 // K steps per pipeline stage: the largest divisor of the step count up to 2
-// (gate and up: two matrices) or 8 (down), so that two stages of weights fit
-// in registers next to each other without spilling.
+// (gate and up: two matrices) or 3 (down, three workgroups per CU), so that
+// two stages of weights fit in registers next to each other without spilling.
 template <int FMT, int MODE, bool A4>
 hipError_t launch_gemm(const BatchedArgs& a, hipStream_t s) {
   const int nks = (MODE == 0 ? a.H : a.I) / kKS;
-  const int cap = MODE == 0 ? 2 : 8;
+  const int cap = MODE == 0 ? 2 : 3;
   int ks = 1;
   for (int d = cap; d >= 1; --d)
     if (nks % d == 0) {
@@ -776,11 +782,6 @@ hipError_t launch_gemm(const BatchedArgs& a, hipStream_t s) {
       break;
     }
   switch (ks) {
-    case 8: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 2 : 8), A4>(a, s);
-    case 7: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 1 : 7), A4>(a, s);
-    case 6: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 2 : 6), A4>(a, s);
-    case 5: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 1 : 5), A4>(a, s);
-    case 4: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 2 : 4), A4>(a, s);
     case 3: return launch_gemm_ks<FMT, MODE, (MODE == 0 ? 1 : 3), A4>(a, s);
     case 2: return launch_gemm_ks<FMT, MODE, 2, A4>(a, s);
     default: return launch_gemm_ks<FMT, MODE, 1, A4>(a, s);
