@@ -439,9 +439,22 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
     if (lane == 63) pre[a.E] = incl;
   }
   __syncthreads();
+  // Tiles per CU, then per workgroup of the CU.  The grid is P workgroups
+  // per CU and workgroups b, b + ncu, b + 2 ncu, ... share CU b % ncu (the
+  // dispatcher fills every CU once before it places a second workgroup on
+  // any), so CU c takes the contiguous tiles [N c / ncu, N (c + 1) / ncu)
+  // and its earlier-placed workgroups, which the CU serves first, take the
+  // larger shares.  Splitting the tiles evenly over blockIdx instead gave
+  // the two workgroups of a CU equal counts, so CUs carried 2 or 4 tiles
+  // at c2 where 3 or 4 suffice.
   const long long ntot = (long long)pre[a.E] * ntiles;
-  const int t0 = (int)(ntot * blockIdx.x / gridDim.x);
-  const int t1 = (int)(ntot * (blockIdx.x + 1) / gridDim.x);
+  const int ncu = a.ncu, P = (int)gridDim.x / ncu;
+  const int cu = (int)blockIdx.x % ncu, rank = (int)blockIdx.x / ncu;
+  if (rank >= P) return;
+  const int cu0 = (int)(ntot * cu / ncu), ncut = (int)(ntot * (cu + 1) / ncu) - cu0;
+  int t0 = cu0;
+  for (int q = 0; q < rank; ++q) t0 += (ncut + P - 1 - q) / P;
+  const int t1 = t0 + (ncut + P - 1 - rank) / P;
   if (t0 >= t1) return;
 
   ItemState it;  // the item being computed
@@ -764,8 +777,10 @@ hipError_t launch_gemm_ks(const BatchedArgs& a, hipStream_t s) {
   // as many workgroups per CU as the occupancy target and the LDS allow
   int per = kWgPerCu[MODE];
   while (per > 1 && (size_t)per * lds > 160 * 1024) --per;
+  BatchedArgs b = a;
+  b.ncu = cu_count();
   return launch_kernel(MODE == 0 ? MOE_KERNEL_BATCHED_GATE_UP : MOE_KERNEL_BATCHED_DOWN,
-                       k_bat_gemm<FMT, MODE, KS, A4>, dim3(per * cu_count()), dim3(64 * kBW), lds, s, a);
+                       k_bat_gemm<FMT, MODE, KS, A4>, dim3(per * b.ncu), dim3(64 * kBW), lds, s, b);
 }
 
 // K steps per pipeline stage: the largest divisor of the step count up to 2

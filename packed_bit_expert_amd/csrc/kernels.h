@@ -56,6 +56,7 @@ struct BatchedArgs {
   uint16_t* ubuf;     // [T][H] the pre-normed input (MOE_FLAG_PRENORM)
   uint16_t* unext;    // [T][H] or null: where the combine writes the pre-norm of out
   bool x_normed;      // ubuf already holds the pre-norm of x
+  int ncu;            // CUs of the device (set by the launcher)
   int T, H, I, K, E;
   uint32_t flags;
   float eps;
