@@ -1,0 +1,96 @@
+"""GPU: edge cases of the batched (sorted, MFMA) path.
+
+"LFM2.5-24B-A2B -- Packed MXFP4 Inference", "Grouped top-4 expert
+execution": the (token, slot) pairs of a call are grouped by expert and each
+selected expert's packed weights are read once.  Two situations the workload
+tests do not reach:
+
+* more than 256 pairs (the workgroups hold the first 256 routing ids in
+  registers and read the rest from memory) with hot experts of more than 16
+  pairs, which take several passes of 16 token rows over the same weights;
+* the layer stack at H = 4096, where one workgroup per token cannot finish a
+  row's pre-norm inside the combine, so a separate pre-norm launch follows it.
+
+Each case is compared with the oracle under the stated tolerance; the stack
+must also equal the chained single-layer calls bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+from packed_bit_expert_amd import moe as M
+from packed_bit_expert_amd import synth as S
+from packed_bit_expert_amd.residency import ResidentExperts
+from tests import gpu_helpers as GH
+
+pytestmark = pytest.mark.gpu
+LFM = S.LFM24B
+WIDE = S.Shape(hidden=4096, inter=512, experts=8, top_k=2, layers=3)
+
+
+def banner(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def layer_mx():
+    banner("upload LFM 2048/1536 E8M0 layer 3")
+    return GH.Layer(LFM, S.FMT_E8M0_G32, 3)
+
+
+@pytest.mark.parametrize("w4a4", [False, True])
+def test_many_pairs_and_multi_pass_experts(layer_mx, w4a4):
+    T = 150
+    banner(f"T={T} ({4 * T} pairs), Zipf routing, w4a4={w4a4}")
+    x = S.activations(9, 3, 0, T, LFM.hidden)
+    ids, rw = S.routing_zipf(9, 3, 0, T, LFM.experts, LFM.top_k)
+    counts = np.bincount(ids.ravel(), minlength=LFM.experts)
+    assert ids.size > 256 and counts.max() > 32, "the case must reach the paths it names"
+    flags = M.FLAG_W4A4 if w4a4 else 0
+    out, st = layer_mx.gpu(x, ids, rw, flags=flags)
+    assert st == 0
+    GH.compare(out, layer_mx.oracle(x, ids, rw, w4a4=w4a4), f"out T={T} w4a4={w4a4}")
+
+
+def test_wide_hidden_stack():
+    sh = WIDE
+    assert M.moe_w4a16_shape_supported(sh.hidden, sh.inter)
+    banner(f"stack of {sh.layers} layers at H={sh.hidden} I={sh.inter}, T=6")
+    store = ResidentExperts(sh, S.FMT_E8M0_G32, sh.layers).fill_synthetic()
+    T, L = 6, sh.layers
+    x = S.activations(4, 0, 0, T, sh.hidden)
+    routes = [S.routing_uniform(4, l, 0, T, sh.experts, sh.top_k) for l in range(L)]
+    ids = np.stack([r[0] for r in routes])
+    rw = np.stack([r[1] for r in routes])
+    # the one-call stack
+    out = torch.empty((T, sh.hidden), dtype=torch.bfloat16, device=GH.dev())
+    cfg = M.make_cfg(T, sh.hidden, sh.inter, sh.experts, sh.top_k, prenorm_eps=GH.EPS)
+    ws = torch.zeros(M.moe_w4a16_workspace_bytes(cfg), dtype=torch.uint8, device=GH.dev())
+    cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), ws.numel()
+    M.moe_w4a16_stack_forward(L, GH.bf16_dev(x), GH.i32_dev(ids), GH.bf16_dev(rw), store.wtab,
+                              store.stab, None, out, cfg)
+    torch.cuda.synchronize()
+    got = GH.bits_host(out)
+    # the same layers as single calls, each on the previous call's output
+    h = GH.bf16_dev(x)
+    for l in range(L):
+        wt, stb, _ = store.layer_tables(l)
+        o = torch.empty_like(h)
+        c = M.make_cfg(T, sh.hidden, sh.inter, sh.experts, sh.top_k, flags=M.FLAG_PRENORM,
+                       residual=h, prenorm_eps=GH.EPS)
+        w2 = torch.zeros(M.moe_w4a16_workspace_bytes(c), dtype=torch.uint8, device=GH.dev())
+        c.workspace, c.workspace_bytes = w2.data_ptr(), w2.numel()
+        M.moe_w4a16_forward(h, GH.i32_dev(ids[l]), GH.bf16_dev(rw[l]), wt, stb, o, c)
+        h = o
+    torch.cuda.synchronize()
+    assert np.array_equal(got, GH.bits_host(h)), "stack call == chained single-layer calls"
+    # every layer against the oracle, on the oracle chain's input
+    hh = x
+    for l in range(L):
+        lay = GH.Layer(sh, S.FMT_E8M0_G32, l, store=store, l=l)
+        nxt = lay.oracle(hh, ids[l], rw[l], residual=hh, prenorm=True)
+        g, st = lay.gpu(hh, ids[l], rw[l], residual=hh, flags=M.FLAG_PRENORM)
+        assert st == 0
+        GH.compare(g, nxt, f"wide layer {l}")
+        hh = nxt
+    GH.compare(got, hh, "wide stack free-running", check=False)
