@@ -7,13 +7,17 @@
 //      pairs with a stable on-device scan of the ids (no id or count ever
 //      reaches the host: "GPU routing inside resident-layer graphs" of the
 //      MXFP4 card); k_sort is the same grouping as a stand-alone hook;
-//   2. k_bat_gemm<MODE 0>: per (expert, 64-row tile) workgroup, the expert's
-//      token rows are staged in LDS, packed gate and up rows are dequantised
-//      to BF16 MFMA operands in registers (exact, no BF16 copy in memory),
-//      v_mfma_f32_16x16x32_bf16 accumulates in FP32, and the epilogue writes
-//      h = bf16(silu(bf16 g) * bf16 u) per pair;
-//   3. k_bat_gemm<MODE 1>: the same for down, writing y per (token, slot);
-//   4. k_combine: the slot-order BF16 combine per token (+ residual).
+//   2. with MOE_FLAG_PRENORM, k_prenorm: the weightless RMS pre-norm of x,
+//      once per call (in the layer stack the previous layer's combine has
+//      already written it);
+//   3. k_bat_gemm<MODE 0>: persistent workgroups walk (expert pass, 64-row
+//      tile) work: the pass's token rows are staged in LDS, packed gate and up
+//      rows are dequantised to BF16 MFMA operands in registers (exact, no
+//      BF16 copy in memory), v_mfma_f32_16x16x32_bf16 accumulates in FP32, and
+//      the epilogue writes h = bf16(silu(bf16 g) * bf16 u) per pair;
+//   4. k_bat_gemm<MODE 1>: the same for down, writing y per (token, slot);
+//   5. k_combine: the slot-order BF16 combine per token (+ residual, and in
+//      the stack the next layer's pre-norm).
 // At these sizes the work is still HBM-bound (12-15 flop per weight byte
 // against a BF16-MFMA ridge near 312): MFMA removes the multiply-adds from
 // the VALU, which is left with the dequantisation.
@@ -342,11 +346,11 @@ __device__ __forceinline__ void stage_rows(const BatchedArgs& a, const int* lp, 
 // The work of one call is a list of items -- (expert e, pass p): up to 16
 // of e's (token, slot) pairs, in order -- times 64-row tiles of the output;
 // a tile's contraction is split into stages of KS K-steps.  The grid is
-// persistent (two workgroups per CU); workgroup b takes the contiguous tiles
-// [b N / G, (b + 1) N / G), so consecutive tiles mostly share an item and its
+// persistent (kWgPerCu workgroups per CU) and takes the tiles CU by CU in
+// contiguous ranges, so consecutive tiles mostly share an item and its
 // staged token rows.  The stages of a workgroup form one software pipeline
 // over two register buffers: the weights of stage g + 1 are issued before
-// the MFMAs of stage g, so a wave always has about one tile of weights in
+// the MFMAs of stage g, so a wave always has about one stage of weights in
 // flight and HBM sees a steady stream instead of one burst per workgroup.
 struct ItemState {
   int e, p, mcnt;
