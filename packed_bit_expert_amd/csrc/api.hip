@@ -71,7 +71,7 @@ bool capturing(hipStream_t s) {
 constexpr int kStackGroup = 64;  // layers whose routing slots are resolved in one pass
 
 struct Layout {
-  size_t hbuf, ybuf, ping, scratch, ubuf, logits, rcount, slots, total;
+  size_t hbuf, hq, ybuf, ping, scratch, ubuf, logits, rcount, slots, total;
 };
 
 Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
@@ -79,6 +79,8 @@ Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
   size_t off = kCtrlBytes;
   L.hbuf = off;
   off += align256((size_t)(T * K * I) * 2);
+  L.hq = off;  // batched W4A4: h as MXFP4 rows (codes, scales, 16-byte padded)
+  off += align256((size_t)(T * K) * ((I / 2 + I / 32 + 15) & ~(int64_t)15));
   L.ybuf = off;
   off += align256((size_t)(T * K * H) * 2);
   L.ping = off;
@@ -276,6 +278,7 @@ int run_layer(const moe_w4a16_cfg* c, const Call& k, const SlotRef* pre = nullpt
   a.dy = d ? (uint16_t*)d->y : nullptr;
   a.err = err;
   a.ubuf = (uint16_t*)(ws + L.ubuf);
+  a.hq = ws + L.hq;
   a.unext = k.norm_out ? a.ubuf : nullptr;
   a.x_normed = k.x_normed;
   a.T = T;

@@ -236,16 +236,43 @@ __device__ __forceinline__ void wstep_mfma4(const WStep<MOE_SCALE_E8M0_G32, NMAT
   }
 }
 
-// MXFP4 quantisation of the staged token rows, in place (W4A4).  Per block of
-// 32 values: E8M0 code c = max(E - 2, 0) with E the BF16 exponent field of
+// MXFP4 quantisation of one block of 32 BF16 values (W4A4), packed two per
+// word in w; returns the 16 code bytes and sets sc.  E8M0 code c = max(E - 2, 0) with E the BF16 exponent field of
 // the block's largest magnitude (so X = 2^(c - 127) = 2^(floor(log2 amax) -
 // 2), clamped at 2^-127; a zero block gets 0), then each element's code is the
 // number of E2M1 rounding thresholds its magnitude r = |v| / X passes: the
 // midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5, counted inclusively where
 // the tie goes up to the even code (0.75, 1.75, 3.5) and exclusively where it
 // stays on the even code below; past 5 everything is 6.  The sign bit is
-// copied.  Row r becomes its Kd / 2 packed code bytes followed by Kd / 32
-// scale bytes.  One wave owns a row and reads all of it before writing.
+// copied.
+__device__ __forceinline__ uint4 mxfp4_block(const uint32_t (&w)[16], uint32_t& sc) {
+  uint32_t amax = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) amax = max(amax, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+  const uint32_t ex = amax >> 7;
+  sc = ex > 2u ? ex - 2u : 0u;
+  const float inv = __uint_as_float((254u - sc) << 23);  // 2^(127 - sc) = 1 / X
+  uint32_t packed[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const uint32_t bits = (k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xFFFFu);
+    const float m = __uint_as_float((bits & 0x7FFFu) << 16) * inv;
+    uint32_t c = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
+                 (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) +
+                 (uint32_t)(m > 5.0f);
+    c |= (bits >> 12) & 8u;
+    packed[k >> 3] |= c << (4 * (k & 7));
+  }
+  return make_uint4(packed[0], packed[1], packed[2], packed[3]);
+}
+
+// Bytes of one MXFP4 row of K values: K / 2 codes, K / 32 scales, padded to
+// 16 bytes (the unit of the direct LDS loads).
+__host__ __device__ constexpr int mxfp4_row_bytes(int K) { return (K / 2 + K / 32 + 15) & ~15; }
+
+// MXFP4 quantisation of the staged token rows, in place: row r becomes its
+// Kd / 2 packed code bytes followed by Kd / 32 scale bytes.  One wave owns a
+// row and reads all of it before writing.
 __device__ __forceinline__ void quant_rows_mxfp4(uint16_t* xs, int ldx, int Kd, int mcnt, int wave,
                                                  int lane) {
   const int nblk = Kd / 32;  // at most 128
@@ -267,24 +294,8 @@ __device__ __forceinline__ void quant_rows_mxfp4(uint16_t* xs, int ldx, int Kd, 
       const uint32_t w[16] = {v[i][0].x, v[i][0].y, v[i][0].z, v[i][0].w, v[i][1].x, v[i][1].y,
                               v[i][1].z, v[i][1].w, v[i][2].x, v[i][2].y, v[i][2].z, v[i][2].w,
                               v[i][3].x, v[i][3].y, v[i][3].z, v[i][3].w};
-      uint32_t amax = 0;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) amax = max(amax, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
-      const uint32_t ex = amax >> 7;
-      const uint32_t sc = ex > 2u ? ex - 2u : 0u;
-      const float inv = __uint_as_float((254u - sc) << 23);  // 2^(127 - sc) = 1 / X
-      uint32_t packed[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        const uint32_t bits = (k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xFFFFu);
-        const float m = __uint_as_float((bits & 0x7FFFu) << 16) * inv;
-        uint32_t c = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
-                     (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) +
-                     (uint32_t)(m > 5.0f);
-        c |= (bits >> 12) & 8u;
-        packed[k >> 3] |= c << (4 * (k & 7));
-      }
-      *(uint4*)(row + 16 * b) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+      uint32_t sc;
+      *(uint4*)(row + 16 * b) = mxfp4_block(w, sc);
       row[Kd / 2 + b] = (uint8_t)sc;
     }
   }
@@ -317,29 +328,34 @@ __device__ void collect_pairs(const int32_t* ids, int id0, int npairs, int e, in
 
 // Stage the 16 A rows of a pass into LDS with the gfx950 direct global->LDS
 // load: one wave instruction moves 1 KiB (16 bytes per lane, lane i at
-// base + 16 i); a row tail of 256 elements uses lanes 0..31.  Rows past the
-// pass's pair count are zero-filled with ordinary LDS stores.
-template <int MODE>
+// base + 16 i).  A row is Kd BF16 values (x or h), or, for down under W4A4,
+// the MXFP4 row of h that gate/up wrote (mxfp4_row_bytes(Kd) bytes).  Rows
+// past the pass's pair count are zero-filled with ordinary LDS stores.
+template <int MODE, bool A4>
 __device__ __forceinline__ void stage_rows(const BatchedArgs& a, const int* lp, int mcnt, int Kd,
                                            int ldx, uint16_t* xs, int wave, int lane) {
-  const int nch = (Kd + 511) / 512;
+  constexpr bool HQ = MODE == 1 && A4;
+  const int n16 = HQ ? mxfp4_row_bytes(Kd) / 16 : Kd / 8;  // 16-byte units per row
+  const int nch = (n16 + 63) / 64;
+  uint8_t* xb = (uint8_t*)xs;
   // Zero rows and the pair indices first: an LDS access between the direct
   // loads would make the compiler wait for all of them.
   for (int q = wave; q < kMC * nch; q += kBW) {
     const int r = q / nch, ch = q - r * nch;
-    if (r >= mcnt && lane * 8 < Kd - ch * 512)
-      *(uint4*)(xs + r * ldx + ch * 512 + lane * 8) = make_uint4(0u, 0u, 0u, 0u);
+    if (r >= mcnt && 64 * ch + lane < n16)
+      *(uint4*)(xb + (size_t)r * ldx * 2 + 1024 * ch + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
   }
   const int mine = lp[lane < mcnt ? lane : 0];  // lane r < mcnt holds row r's pair
   for (int q = wave; q < mcnt * nch; q += kBW) {
     const int r = q / nch, ch = q - r * nch;
     const int pair = __builtin_amdgcn_readlane(mine, r);
-    const uint16_t* src = (MODE == 0 ? a.x + (size_t)(pair / a.K) * Kd : a.hbuf + (size_t)pair * Kd) +
-                          ch * 512 + lane * 8;
-    if (lane * 8 < Kd - ch * 512)
-      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(xs + r * ldx + ch * 512),
-                                       16, 0, 0);
+    const uint8_t* row = HQ ? a.hq + (size_t)pair * mxfp4_row_bytes(Kd)
+                            : (const uint8_t*)(MODE == 0 ? a.x + (size_t)(pair / a.K) * Kd
+                                                         : a.hbuf + (size_t)pair * Kd);
+    if (64 * ch + lane < n16)
+      __builtin_amdgcn_global_load_lds(
+          (__attribute__((address_space(1))) void*)(row + 1024 * ch + 16 * lane),
+          (__attribute__((address_space(3))) void*)(xb + (size_t)r * ldx * 2 + 1024 * ch), 16, 0, 0);
   }
 }
 
@@ -393,6 +409,8 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
   const uint8_t** tw = (const uint8_t**)((char*)lds + tab_off);
   const uint8_t** ts = tw + a.E;
   float* tt = (float*)(ts + a.E);
+  // gate/up under W4A4: one tile's h, [16 tokens][64 rows] BF16
+  uint16_t* hl = (uint16_t*)((char*)lds + ((tab_off + a.E * (2 * (int)sizeof(void*) + 4) + 15) & ~15));
   const int npairs = a.T * a.K;
 
   // 1. the items: per-expert pair counts, then the prefix of their passes
@@ -482,7 +500,7 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
     it.tscale = (double)tt[e];
     it.ok = aligned(e);
     collect_pairs(a.ids, id0, npairs, e, kMC * it.p, list, wcnt);
-    stage_rows<MODE>(a, list, it.mcnt, Kd, ldx, xs, wave, lane);
+    stage_rows<MODE, A4>(a, list, it.mcnt, Kd, ldx, xs, wave, lane);
   };
   // row pointers of this lane for tile column block j of the current item
   auto rows_for = [&](int j) {
@@ -524,7 +542,7 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
         for (int k = lane; k < Kd; k += 64) a.du[(size_t)t * Kd + k] = row[k];
       }
     }
-    if constexpr (A4) {
+    if constexpr (A4 && MODE == 0) {  // down's rows of h arrive quantised
       quant_rows_mxfp4(xs, ldx, Kd, it.mcnt, wave, lane);
       lds_barrier();
     }
@@ -560,6 +578,7 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
     if (st != nst - 1) return;
     // epilogue: lane holds D[m = 4 gl + i][n] of the M tile
     const int n = (tile % ntiles) * kBN + wave * 16 + ln;
+    if constexpr (MODE == 0 && A4) lds_barrier();  // wave 0 has read the last tile's h
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 4 * gl + i;
@@ -570,7 +589,8 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
           const uint16_t ub = f64_to_bf16(acc[1][i] * it.tscale);
           const uint16_t h = silu_mul_bf16(gb, ub);
           const size_t o = (size_t)pair * a.I + n;
-          a.hbuf[o] = h;
+          if constexpr (A4) hl[m * 64 + wave * 16 + ln] = h;
+          else a.hbuf[o] = h;
           if (a.dg) a.dg[o] = gb;
           if (a.dv) a.dv[o] = ub;
           if (a.dh) a.dh[o] = h;
@@ -580,6 +600,24 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
           a.ybuf[o] = y;
           if (a.dy) a.dy[o] = y;
         }
+      }
+    }
+    if constexpr (MODE == 0 && A4) {
+      // down's MXFP4 rows of h, once per tile: a lane per 32-row block of a
+      // token (two per token in the 64-row tile), from the tile in LDS
+      lds_barrier();
+      if (wave == 0 && lane < 2 * it.mcnt && it.ok) {
+        const int m = lane >> 1, half = lane & 1;
+        const uint4* src = (const uint4*)(hl + m * 64 + 32 * half);
+        const uint4 v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
+        const uint32_t w[16] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
+                                v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
+        uint32_t sc;
+        const uint4 codes = mxfp4_block(w, sc);
+        const int n0 = (tile % ntiles) * kBN + 32 * half;  // the block's first row
+        uint8_t* row = a.hq + (size_t)list[m] * mxfp4_row_bytes(a.I);
+        *(uint4*)(row + n0 / 2) = codes;
+        row[a.I / 2 + n0 / 32] = (uint8_t)sc;
       }
     }
 #pragma unroll
@@ -770,8 +808,10 @@ template <int FMT, int MODE, int KS, bool A4>
 hipError_t launch_gemm_ks(const BatchedArgs& a, hipStream_t s) {
   const int Kd = MODE == 0 ? a.H : a.I;
   const size_t lds = (size_t)kMC * (Kd + 8) * 2 + (size_t)(kMC + 2 * a.E + 1 + kBW) * 4 + 8 +
-                     (size_t)a.E * (2 * sizeof(void*) + sizeof(float));
-  // The largest shape a check admits (K 4096, 1024 experts) needs 156.3 KiB.
+                     (size_t)a.E * (2 * sizeof(void*) + sizeof(float)) +
+                     (MODE == 0 && A4 ? 16 + 1024 * 2 : 0);
+  // The largest shape a check admits (K 4096, 1024 experts) needs 156.3 KiB,
+  // 158.3 KiB for gate/up under W4A4.
   static size_t allowed = 0;  // benign race: the value only grows towards the same bound
   if (lds > allowed) {
     hipError_t e = allow_lds(k_bat_gemm<FMT, MODE, KS, A4>, lds);

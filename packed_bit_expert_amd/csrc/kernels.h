@@ -51,6 +51,7 @@ struct BatchedArgs {
   uint16_t* out;
   uint16_t* hbuf;     // [T * K][I]
   uint16_t* ybuf;     // [T * K][H]
+  uint8_t* hq;        // [T * K][mxfp4_row_bytes(I)]: h as MXFP4 rows (W4A4)
   uint16_t *du, *dg, *dv, *dh, *dy;
   int* err;
   uint16_t* ubuf;     // [T][H] the pre-normed input (MOE_FLAG_PRENORM)
