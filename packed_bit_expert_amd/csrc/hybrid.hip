@@ -13,7 +13,9 @@
 // outside graph capture.
 #include <string.h>
 
+#include <algorithm>
 #include <list>
+#include <thread>
 #include <unordered_map>
 #include <vector>
 
@@ -55,8 +57,9 @@ void release(moe_w4a16_hybrid* h) {
   delete h;
 }
 
-// The pinned slot holding `key`, copying the triplet in from the checkpoint
-// on a miss (evicting the least recently used entry when full).
+// The pinned slot of `key` under LRU: its slot on a hit; on a miss a free
+// slot or the least recently used entry's, which the caller fills from the
+// checkpoint.
 int cache_slot(moe_w4a16_hybrid* h, const void* key, bool* hit) {
   auto it = h->where.find(key);
   if (it != h->where.end()) {
@@ -73,10 +76,30 @@ int cache_slot(moe_w4a16_hybrid* h, const void* key, bool* hit) {
     h->where.erase(h->order.back().first);
     h->order.pop_back();
   }
-  memcpy(h->pinned + (size_t)slot * h->triplet, key, (size_t)h->triplet);
   h->order.emplace_front(key, slot);
   h->where[key] = h->order.begin();
   return slot;
+}
+
+// n copies of `bytes` each (dst[i] <- src[i]), split over up to four host
+// threads in contiguous pieces of the concatenated copies.
+void parallel_copy(const std::vector<uint8_t*>& dst, const std::vector<const uint8_t*>& src,
+                   size_t bytes) {
+  const size_t total = dst.size() * bytes;
+  if (total == 0) return;
+  const int nt = total >= (4u << 20) ? 4 : 1;
+  auto work = [&](int t) {
+    size_t lo = total * t / nt, hi = total * (t + 1) / nt;
+    while (lo < hi) {
+      const size_t i = lo / bytes, off = lo % bytes, n = std::min(hi - lo, bytes - off);
+      memcpy(dst[i] + off, src[i] + off, n);
+      lo += n;
+    }
+  };
+  std::vector<std::thread> pool;
+  for (int t = 1; t < nt; ++t) pool.emplace_back(work, t);
+  work(0);
+  for (auto& th : pool) th.join();
 }
 
 }  // namespace
@@ -165,17 +188,36 @@ int moe_w4a16_hybrid_forward(moe_w4a16_hybrid* h, const void* x, const int32_t* 
     slot_of[ex] = st;
     h->last_experts.push_back(ex);
   }
-  // 3. pinned cache (hit) or checkpoint (miss), then one H2D copy each
-  for (size_t r = 0; r < h->last_experts.size(); ++r) {
+  // 3. the cache decides hits and slots in request order; the hits' H2D
+  // copies start at once, then the misses' slots are filled from the
+  // checkpoint (on several host threads, while the hits' copies run) and
+  // copied too.  No entry used in this call can be evicted by it (the cache
+  // holds at least staging_slots triplets), and the id copy above waited for
+  // every earlier copy out of the cache.
+  const size_t nreq = h->last_experts.size();
+  std::vector<int> cslot(nreq);
+  std::vector<uint8_t*> fill_dst;
+  std::vector<const uint8_t*> fill_src;
+  for (size_t r = 0; r < nreq; ++r) {
     const int ex = h->last_experts[r];
     bool hit = false;
-    const int cs = cache_slot(h, host_src[ex], &hit);
+    cslot[r] = cache_slot(h, host_src[ex], &hit);
     h->last_hits.push_back(hit ? 1 : 0);
     (hit ? h->hits : h->misses)++;
-    e = hipMemcpyAsync(h->staging + r * h->triplet, h->pinned + (size_t)cs * h->triplet,
-                       (size_t)h->triplet, hipMemcpyHostToDevice, s);
-    if (e != hipSuccess) return herr(e, "expert H2D copy");
-    h->h2d_bytes += h->triplet;
+    if (!hit) {
+      fill_dst.push_back(h->pinned + (size_t)cslot[r] * h->triplet);
+      fill_src.push_back((const uint8_t*)host_src[ex]);
+    }
+  }
+  for (int pass = 0; pass < 2; ++pass) {
+    if (pass == 1) parallel_copy(fill_dst, fill_src, (size_t)h->triplet);
+    for (size_t r = 0; r < nreq; ++r) {
+      if (h->last_hits[r] != (pass == 0 ? 1 : 0)) continue;
+      e = hipMemcpyAsync(h->staging + r * h->triplet, h->pinned + (size_t)cslot[r] * h->triplet,
+                         (size_t)h->triplet, hipMemcpyHostToDevice, s);
+      if (e != hipSuccess) return herr(e, "expert H2D copy");
+      h->h2d_bytes += h->triplet;
+    }
   }
   // 4. the layer's pointer tables: resident experts in place, routed CPU
   // experts in their staging slots, other CPU experts (never read) at slot 0
