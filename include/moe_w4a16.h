@@ -197,7 +197,9 @@ int moe_w4a16_forward_debug(const void* x, const int32_t* expert_ids, const void
  *   tensor_scales            device FP32 [L][E][2] (E4M3) or NULL (E8M0)
  * At T = 1 every layer is two decode launches (the routing slots of up to 64
  * layers are resolved to expert addresses by one extra launch); otherwise
- * each layer is one batched sequence.
+ * each layer is one batched sequence (gate/up GEMM, down GEMM, combine),
+ * whose combine also writes the next layer's pre-normed input into the
+ * workspace, so only the first layer has a pre-norm launch.
  */
 int moe_w4a16_stack_forward(int32_t num_layers, const void* x, const int32_t* expert_ids,
                             const void* route_w, const void* const* packed_weights,
