@@ -97,7 +97,12 @@ void parallel_copy(const std::vector<uint8_t*>& dst, const std::vector<const uin
     }
   };
   std::vector<std::thread> pool;
-  for (int t = 1; t < nt; ++t) pool.emplace_back(work, t);
+  int spawned = 1;
+  try {
+    for (; spawned < nt; ++spawned) pool.emplace_back(work, spawned);
+  } catch (...) {  // no thread to be had: the calling thread copies the rest
+  }
+  for (int t = spawned; t < nt; ++t) work(t);
   work(0);
   for (auto& th : pool) th.join();
 }
