@@ -387,6 +387,12 @@ __device__ __forceinline__ int expert_of(const int* pre, int E, int it) {
 
 template <int FMT, int MODE, int KS, bool A4>
 __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedArgs a) {
+  // the arguments of the prologue's loads, fetched in one scalar batch (the
+  // compiler would otherwise fetch them in dependent rounds near use)
+  asm volatile("" ::"s"(a.ids), "s"(a.wtab), "s"(a.stab), "s"(a.tsc), "s"(a.x), "s"(a.hbuf),
+               "s"(a.ybuf), "s"(a.hq), "s"(a.du), "s"(a.dg), "s"(a.dv), "s"(a.dh), "s"(a.dy),
+               "s"(a.err), "s"(a.T), "s"(a.K), "s"(a.E), "s"(a.I), "s"(a.H), "s"(a.ncu),
+               "s"(a.flags));
   static_assert(!A4 || FMT == MOE_SCALE_E8M0_G32, "W4A4 pairs E8M0 scales on both operands");
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   constexpr int NMAT = MODE == 0 ? 2 : 1;
@@ -413,7 +419,10 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
   uint16_t* hl = (uint16_t*)((char*)lds + ((tab_off + a.E * (2 * (int)sizeof(void*) + 4) + 15) & ~15));
   const int npairs = a.T * a.K;
 
-  // 1. the items: per-expert pair counts, then the prefix of their passes
+  // 1. the items: per-expert pair counts, then the prefix of their passes.
+  // The first 256 ids are requested with the expert tables, so that both
+  // round trips overlap.
+  const int id0 = tid < npairs ? a.ids[tid] : -1;
   for (int e = tid; e < a.E; e += 64 * kBW) {
     cnt[e] = 0;
     tw[e] = a.wtab[e];
@@ -422,7 +431,6 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
   }
   __syncthreads();
   bool bad = false;
-  const int id0 = tid < npairs ? a.ids[tid] : -1;
   for (int p = tid; p < npairs; p += 64 * kBW) {
     const int e = p == tid ? id0 : a.ids[p];
     if ((unsigned)e < (unsigned)a.E) atomicAdd(&cnt[e], 1);

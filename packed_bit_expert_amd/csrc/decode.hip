@@ -160,6 +160,10 @@ __device__ __forceinline__ SlotRef load_slot(const SlotRef* p) {
 // straight-line and each chunk waits only for its own load.
 template <int H, int FMT, bool PRENORM, bool DUMP>
 __global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
+  // every argument the first loads depend on, fetched in one scalar batch
+  // (the compiler would otherwise fetch them in dependent rounds near use)
+  asm volatile("" ::"s"(a.x), "s"(a.pre), "s"(a.slots), "s"(a.hbuf), "s"(a.T), "s"(a.I),
+               "s"(a.K), "s"(a.eps));
   using S = GuShape<H>;
   using M = typename S::M;
   constexpr int LPR = M::LPR, CPL = M::CPL, RPS = M::RPS, NS = S::NS, RW = S::RW;
@@ -312,6 +316,9 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
 // then takes its slices from there instead of re-reading them from L2.
 template <int H, int I, int FMT, bool DUMP>
 __global__ __launch_bounds__(256) void k_dec_down(DecodeArgs a) {
+  // every argument the first loads depend on, fetched in one scalar batch
+  asm volatile("" ::"s"(a.pre), "s"(a.slots), "s"(a.hbuf), "s"(a.rw), "s"(a.residual),
+               "s"(a.out), "s"(a.T), "s"(a.K));
   using D = DnShape<I>;
   using M = typename D::M;
   constexpr int LPR = M::LPR, CPL = M::CPL, RPS = M::RPS, NS = D::NS, ROWS = D::ROWS;

@@ -109,6 +109,9 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ x,
                                                 int K, float eps, double* logits, uint32_t* count,
                                                 int32_t* __restrict__ ids,
                                                 uint16_t* __restrict__ rw) {
+  // every argument fetched in one scalar batch
+  asm volatile("" ::"s"(x), "s"(wr), "s"(bias), "s"(H), "s"(E), "s"(K), "s"(eps), "s"(logits),
+               "s"(count), "s"(ids), "s"(rw));
   __shared__ __attribute__((aligned(16))) uint16_t us[2048];
   __shared__ double red[4], lgs[4];
   __shared__ int last;
