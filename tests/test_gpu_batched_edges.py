@@ -2,14 +2,17 @@
 
 "LFM2.5-24B-A2B -- Packed MXFP4 Inference", "Grouped top-4 expert
 execution": the (token, slot) pairs of a call are grouped by expert and each
-selected expert's packed weights are read once.  Two situations the workload
+selected expert's packed weights are read once.  Situations the workload
 tests do not reach:
 
 * more than 256 pairs (the workgroups hold the first 256 routing ids in
   registers and read the rest from memory) with hot experts of more than 16
   pairs, which take several passes of 16 token rows over the same weights;
 * the layer stack at H = 4096, where one workgroup per token cannot finish a
-  row's pre-norm inside the combine, so a separate pre-norm launch follows it.
+  row's pre-norm inside the combine, so a separate pre-norm launch follows it;
+* the largest expert count and top-k the ABI admits (1024 experts, top-8), on
+  both paths;
+* every token routed to the same four experts (three passes each).
 
 Each case is compared with the oracle under the stated tolerance; the stack
 must also equal the chained single-layer calls bit for bit.
@@ -94,3 +97,36 @@ def test_wide_hidden_stack():
         GH.compare(g, nxt, f"wide layer {l}")
         hh = nxt
     GH.compare(got, hh, "wide stack free-running", check=False)
+
+
+MAXSH = S.Shape(hidden=512, inter=256, experts=1024, top_k=8, layers=1)
+
+
+@pytest.mark.parametrize("T", [1, 9])
+def test_most_experts_and_largest_top_k(T):
+    """E = 1024 experts (the largest the ABI admits) and top-8 routing, on the
+    decode path (T = 1) and the batched path (T = 9)."""
+    banner(f"E={MAXSH.experts} top_k={MAXSH.top_k} T={T}")
+    L = GH.Layer(MAXSH, S.FMT_E8M0_G32, 2)
+    x = S.activations(6, 2, T, T, MAXSH.hidden)
+    ids, rw = S.routing_zipf(6, 2, T, T, MAXSH.experts, MAXSH.top_k)
+    r = S.activations(7, 2, T, T, MAXSH.hidden)
+    out, st = L.gpu(x, ids, rw, residual=r)
+    assert st == 0
+    GH.compare(out, L.oracle(x, ids, rw, residual=r), f"E=1024 k=8 T={T}")
+
+
+def test_every_token_the_same_experts(layer_mx):
+    """All 40 tokens pick the same four experts (in rotating slot order):
+    four experts with 40 pairs each, three passes of 16 token rows apiece."""
+    T = 40
+    banner(f"T={T}, every token routed to the same four experts")
+    x = S.activations(8, 3, 1, T, LFM.hidden)
+    base = np.array([5, 9, 2, 60], np.int32)
+    ids = np.stack([np.roll(base, t % 4) for t in range(T)]).astype(np.int32)
+    _, rw = S.routing_uniform(8, 3, 1, T, LFM.experts, LFM.top_k)
+    out, st = layer_mx.gpu(x, ids, rw)
+    assert st == 0
+    GH.compare(out, layer_mx.oracle(x, ids, rw), "same experts")
+    again, _ = layer_mx.gpu(x, ids, rw)
+    assert np.array_equal(out, again)
