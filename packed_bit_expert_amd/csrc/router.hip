@@ -170,7 +170,7 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ x,
   __syncthreads();
   if (tid == 0) {
     for (int w = 0; w < 4; ++w)
-      if (blockIdx.y * 4 + w < E)
+      if ((int)blockIdx.y * 4 + w < E)
         __hip_atomic_store(logits + (size_t)t * E + blockIdx.y * 4 + w, lgs[w], __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     // the logits are device-coherent stores: once they have completed, the
