@@ -15,7 +15,6 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 
-import numpy as np
 import torch
 
 from . import synth

@@ -10,7 +10,6 @@ checkpoint sizes.
 import json
 import os
 
-import numpy as np
 import pytest
 
 from packed_bit_expert_amd import synth as S

@@ -9,7 +9,6 @@ ties, subnormals and overflow.
 import math
 
 import numpy as np
-import pytest
 import torch
 
 from tests import exact_ref as X
