@@ -181,7 +181,7 @@ __device__ __forceinline__ bf16x8 wstep_operand(const WStep<FMT, NMAT>& st, int 
     return fp4x8_scaled_to_bf16x8(w, e4m3_f32((st.s[mt] >> (8 * (d >> 1))) & 255u));
 }
 
-// One K step: 8 MFMAs per matrix on one 16-token tile.  Each MFMA's FP32
+// One K step: 8 MFMAs per matrix on one 16-token tile (E8M0; E4M3 below).  Each MFMA's FP32
 // result (32 exact BF16 products) is added to FP64 accumulators, which keeps
 // the BF16 outputs correctly rounded almost always (as in the decode path).
 // Chaining MFMAs in FP32 instead is cheaper but flips output roundings often
@@ -190,18 +190,48 @@ __device__ __forceinline__ bf16x8 wstep_operand(const WStep<FMT, NMAT>& st, int 
 template <int FMT, int NMAT>
 __device__ __forceinline__ void wstep_mfma(const WStep<FMT, NMAT>& st, const uint16_t* arow,
                                            double (&acc)[2][4]) {
+  if constexpr (FMT == MOE_SCALE_E8M0_G32) {
 #pragma unroll
-  for (int d = 0; d < 8; ++d) {
-    const bf16x8 A = *(const bf16x8*)(arow + 8 * d);
+    for (int d = 0; d < 8; ++d) {
+      const bf16x8 A = *(const bf16x8*)(arow + 8 * d);
 #pragma unroll
-    for (int mt = 0; mt < NMAT; ++mt) {
-      const f32x4 part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          A, wstep_operand<FMT, NMAT>(st, mt, d), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      for (int mt = 0; mt < NMAT; ++mt) {
+        const f32x4 part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            A, wstep_operand<FMT, NMAT>(st, mt, d), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[mt][i] += (double)part[i];
+        for (int i = 0; i < 4; ++i) acc[mt][i] += (double)part[i];
+      }
     }
-    // keeps the scheduler from dequantising many operands ahead (they spill)
-    if constexpr (FMT == MOE_SCALE_E4M3_G16) __builtin_amdgcn_sched_barrier(0);
+  } else {
+    // E4M3: the four lane groups' slices of one MFMA carry four different
+    // scales, whose ratios reach 2^14, and an FP32 sum across them rounds
+    // often enough to break the parity bound where the slots cancel.  Each
+    // lane group's slices get MFMAs of their own (the other lanes give
+    // zeros); MFMAs d = 2j and 2j + 1 of a lane group read one 16-value scale
+    // group, so they are chained in FP32 and added to FP64 once: every FP32
+    // sum stays inside one scale group, as with E8M0.
+    const bf16x8 Z = {};
+    const int q0 = (int)(threadIdx.x & 63) >> 4;  // this lane's group
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 A0 = *(const bf16x8*)(arow + 16 * j);
+      const bf16x8 A1 = *(const bf16x8*)(arow + 16 * j + 8);
+#pragma unroll
+      for (int mt = 0; mt < NMAT; ++mt) {
+        const bf16x8 B0 = wstep_operand<FMT, NMAT>(st, mt, 2 * j);
+        const bf16x8 B1 = wstep_operand<FMT, NMAT>(st, mt, 2 * j + 1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f32x4 ch = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, q0 == q ? B0 : Z,
+                                                              f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          ch = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, q0 == q ? B1 : Z, ch, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mt][i] += (double)ch[i];
+        }
+      }
+      // keeps the scheduler from dequantising many operands ahead (they spill)
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
