@@ -256,9 +256,11 @@ def main():
         torch.cuda.synchronize()
     del buf
 
-    cpu = None
+    cpu = cpu1 = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, shape, args.cpu_seconds, w4a4=w4a4)
+        # the same oracle on one thread, over a shorter sample
+        cpu1 = cpu_baseline(w, shape, args.cpu_seconds / 2, w4a4=w4a4, nthreads=1)
 
     if dominant is not None and "achieved_GBps" in dominant:
         roof = {"bound": "hbm", "achieved": dominant["achieved_GBps"], "peak": HBM_PEAK_GBPS,
@@ -311,6 +313,7 @@ def main():
         "kernels": kernels,
         "hbm_stream_read_GBps": stream_gbps,
         "cpu_baseline": cpu,
+        "cpu_baseline_1thread": cpu1,
     }
     print(json.dumps(res), flush=True)
 
@@ -581,16 +584,17 @@ def workload_name(k):
     }[k]
 
 
-def cpu_baseline(w, shape, target_s, w4a4=False):
-    """The oracle as it stands on this host's cores, on a bounded sample of the
-    workload: layer calls of the workload's batch in the workload's order
-    (consecutive layers of one step, chained through the pre-norm and residual
-    for the stack), until about `target_s` seconds of oracle time."""
+def cpu_baseline(w, shape, target_s, w4a4=False, nthreads=0):
+    """The oracle as it stands on this host's cores (all of them, or
+    `nthreads`), on a bounded sample of the workload: layer calls of the
+    workload's batch in the workload's order (consecutive layers of one step,
+    chained through the pre-norm and residual for the stack), until about
+    `target_s` seconds of oracle time."""
     import numpy as np
 
     from oracle import oracle as O
     from packed_bit_expert_amd import synth as S
-    threads = O.threads_available()
+    threads = nthreads or O.threads_available()
     T = w.tokens
     busy = 0.0
     calls = 0
@@ -613,7 +617,7 @@ def cpu_baseline(w, shape, target_s, w4a4=False):
         out = O.moe_forward(h, ids, rw, nib, sc, hidden=shape.hidden, inter=shape.inter,
                             num_experts=shape.experts, fmt=w.fmt, tensor_scales=ts,
                             residual=h if w.chained else None, prenorm=w.chained, eps=EPS,
-                            w4a4=w4a4)
+                            w4a4=w4a4, nthreads=threads)
         busy += time.perf_counter() - t0
         if w.chained:
             h = out
