@@ -56,7 +56,7 @@ def main():
         pmc_summary(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(expert-parallel sharding is a design note, not code). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
