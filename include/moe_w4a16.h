@@ -313,7 +313,9 @@ int moe_w4a16_delay(uint32_t microseconds, void* stream);
 #define MOE_KERNEL_ZERO 10           /* workspace fill */
 #define MOE_KERNEL_DELAY 11          /* moe_w4a16_delay */
 #define MOE_KERNEL_ROUTER 12         /* router projection, sigmoid, bias, top-k, coefficients */
-#define MOE_KERNEL_PRENORM 13        /* batched: weightless RMS pre-norm of the layer input */
+#define MOE_KERNEL_PRENORM 13        /* batched: weightless RMS pre-norm of the layer input
+                                        (under W4A4 also its MXFP4 rows) */
+#define MOE_KERNEL_QUANT_X 14        /* batched W4A4 without pre-norm: x as MXFP4 rows */
 
 /*
  * Kernel timing (measurement only).  After moe_w4a16_timing_begin(capacity)

@@ -71,7 +71,7 @@ bool capturing(hipStream_t s) {
 constexpr int kStackGroup = 64;  // layers whose routing slots are resolved in one pass
 
 struct Layout {
-  size_t hbuf, hq, ybuf, ping, scratch, ubuf, logits, rcount, slots, total;
+  size_t hbuf, hq, ybuf, ping, scratch, ubuf, xq, logits, rcount, slots, total;
 };
 
 Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
@@ -89,6 +89,8 @@ Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
   off += align256((size_t)(T * H) * 2);
   L.ubuf = off;  // batched: the pre-normed layer input
   off += align256((size_t)(T * H) * 2);
+  L.xq = off;  // batched W4A4: the pre-normed layer input as MXFP4 rows
+  off += align256((size_t)T * ((H / 2 + H / 32 + 15) & ~(int64_t)15));
   L.logits = off;  // router logits, FP64 [T][E]
   off += align256((size_t)(T * E) * 8);
   L.rcount = off;  // router: waves done per token (zero between calls)
@@ -279,6 +281,8 @@ int run_layer(const moe_w4a16_cfg* c, const Call& k, const SlotRef* pre = nullpt
   a.err = err;
   a.ubuf = (uint16_t*)(ws + L.ubuf);
   a.hq = ws + L.hq;
+  a.xqbuf = ws + L.xq;
+  a.xq = nullptr;
   a.unext = k.norm_out ? a.ubuf : nullptr;
   a.x_normed = k.x_normed;
   a.T = T;

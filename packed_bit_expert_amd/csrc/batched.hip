@@ -275,25 +275,60 @@ __device__ __forceinline__ void wstep_mfma4(const WStep<MOE_SCALE_E8M0_G32, NMAT
 // the tie goes up to the even code (0.75, 1.75, 3.5) and exclusively where it
 // stays on the even code below; past 5 everything is 6.  The sign bit is
 // copied.
+__device__ __forceinline__ uint32_t mxfp4_scale_code(uint32_t amax) {
+  const uint32_t ex = amax >> 7;
+  return ex > 2u ? ex - 2u : 0u;
+}
+
+// The E2M1 code of one BF16 value (bits) given inv = 1 / X = 2^(127 - sc).
+__device__ __forceinline__ uint32_t mxfp4_code(uint32_t bits, float inv) {
+  const float m = __uint_as_float((bits & 0x7FFFu) << 16) * inv;
+  const uint32_t c = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
+                     (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) +
+                     (uint32_t)(m > 5.0f);
+  return c | ((bits >> 12) & 8u);
+}
+
 __device__ __forceinline__ uint4 mxfp4_block(const uint32_t (&w)[16], uint32_t& sc) {
   uint32_t amax = 0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) amax = max(amax, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
-  const uint32_t ex = amax >> 7;
-  sc = ex > 2u ? ex - 2u : 0u;
+  sc = mxfp4_scale_code(amax);
   const float inv = __uint_as_float((254u - sc) << 23);  // 2^(127 - sc) = 1 / X
   uint32_t packed[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
     const uint32_t bits = (k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xFFFFu);
-    const float m = __uint_as_float((bits & 0x7FFFu) << 16) * inv;
-    uint32_t c = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
-                 (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) +
-                 (uint32_t)(m > 5.0f);
-    c |= (bits >> 12) & 8u;
-    packed[k >> 3] |= c << (4 * (k & 7));
+    packed[k >> 3] |= mxfp4_code(bits, inv) << (4 * (k & 7));
   }
   return make_uint4(packed[0], packed[1], packed[2], packed[3]);
+}
+
+// The same quantisation spread over four consecutive lanes that hold eight
+// consecutive values each (v, values 8 k8 .. 8 k8 + 7 of a row of K): the
+// block's largest magnitude over the four lanes, then each lane's eight codes,
+// one word of the block's 16 code bytes; the first lane of the four writes
+// the E8M0 byte.  Every lane of the wave must call it (the exchange is DPP).
+__device__ __forceinline__ void mxfp4_store8(uint4 v, int k8, uint8_t* row, int K, bool live) {
+  const int lane = (int)(threadIdx.x & 63);
+  const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+  uint32_t amax = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) amax = max(amax, max(w4[q] & 0x7FFFu, (w4[q] >> 16) & 0x7FFFu));
+  amax = max(amax, xor_lane_u32<1>(amax, lane));
+  amax = max(amax, xor_lane_u32<2>(amax, lane));
+  const uint32_t sc = mxfp4_scale_code(amax);
+  const float inv = __uint_as_float((254u - sc) << 23);
+  uint32_t word = 0u;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t bits = (k & 1) ? (w4[k >> 1] >> 16) : (w4[k >> 1] & 0xFFFFu);
+    word |= mxfp4_code(bits, inv) << (4 * k);
+  }
+  if (live) {
+    *(uint32_t*)(row + 4 * k8) = word;
+    if ((k8 & 3) == 0) row[K / 2 + k8 / 4] = (uint8_t)sc;
+  }
 }
 
 // Bytes of one MXFP4 row of K values: K / 2 codes, K / 32 scales, padded to
@@ -364,7 +399,9 @@ __device__ void collect_pairs(const int32_t* ids, int id0, int npairs, int e, in
 template <int MODE, bool A4>
 __device__ __forceinline__ void stage_rows(const BatchedArgs& a, const int* lp, int mcnt, int Kd,
                                            int ldx, uint16_t* xs, int wave, int lane) {
-  constexpr bool HQ = MODE == 1 && A4;
+  // MXFP4 rows: h under W4A4 (written by gate/up), and x when the pre-norm
+  // that produced it also quantised it (a.xq)
+  const bool HQ = A4 && (MODE == 1 || a.xq != nullptr);
   const int n16 = HQ ? mxfp4_row_bytes(Kd) / 16 : Kd / 8;  // 16-byte units per row
   const int nch = (n16 + 63) / 64;
   uint8_t* xb = (uint8_t*)xs;
@@ -379,9 +416,11 @@ __device__ __forceinline__ void stage_rows(const BatchedArgs& a, const int* lp, 
   for (int q = wave; q < mcnt * nch; q += kBW) {
     const int r = q / nch, ch = q - r * nch;
     const int pair = __builtin_amdgcn_readlane(mine, r);
-    const uint8_t* row = HQ ? a.hq + (size_t)pair * mxfp4_row_bytes(Kd)
-                            : (const uint8_t*)(MODE == 0 ? a.x + (size_t)(pair / a.K) * Kd
-                                                         : a.hbuf + (size_t)pair * Kd);
+    const uint8_t* row =
+        HQ ? (MODE == 1 ? a.hq + (size_t)pair * mxfp4_row_bytes(Kd)
+                        : a.xq + (size_t)(pair / a.K) * mxfp4_row_bytes(Kd))
+           : (const uint8_t*)(MODE == 0 ? a.x + (size_t)(pair / a.K) * Kd
+                                        : a.hbuf + (size_t)pair * Kd);
     if (64 * ch + lane < n16)
       __builtin_amdgcn_global_load_lds(
           (__attribute__((address_space(1))) void*)(row + 1024 * ch + 16 * lane),
@@ -581,8 +620,10 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
       }
     }
     if constexpr (A4 && MODE == 0) {  // down's rows of h arrive quantised
-      quant_rows_mxfp4(xs, ldx, Kd, it.mcnt, wave, lane);
-      lds_barrier();
+      if (!a.xq) {                     // and so do x's when the pre-norm quantised them
+        quant_rows_mxfp4(xs, ldx, Kd, it.mcnt, wave, lane);
+        lds_barrier();
+      }
     }
   };
   double acc[2][4];
@@ -756,12 +797,13 @@ __device__ __forceinline__ uint4 scale8(uint4 v, double rs) {
   return make_uint4(o4[0], o4[1], o4[2], o4[3]);
 }
 
-template <bool NORM>
+template <bool NORM, bool Q>
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
                                                  const uint16_t* __restrict__ rw,
                                                  const uint16_t* __restrict__ residual,
                                                  uint16_t* __restrict__ out, int K, int H,
-                                                 uint16_t* __restrict__ u, float eps) {
+                                                 uint16_t* __restrict__ u, float eps,
+                                                 uint8_t* __restrict__ uq) {
   __shared__ double red[4];
   const int t = blockIdx.y;
   const int m8 = blockIdx.x * 256 + threadIdx.x;
@@ -797,14 +839,19 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
   }
   if constexpr (NORM) {
     const double rs = row_rscale(live ? sq8(o) : 0.0, H, eps, red);
-    if (live) *(uint4*)(u + (size_t)t * H + 8 * m8) = scale8(o, rs);
+    const uint4 uv = scale8(o, rs);
+    if (live) *(uint4*)(u + (size_t)t * H + 8 * m8) = uv;
+    if constexpr (Q) mxfp4_store8(uv, m8, uq + (size_t)t * mxfp4_row_bytes(H), H, live);
   }
 }
 
 // The weightless RMS pre-norm of each row of x: u = bf16(x * rsqrt(mean(x^2)
-// + eps)), FP64; one workgroup per token, H <= 4096.
+// + eps)), FP64; one workgroup per token, H <= 4096.  With Q it also writes
+// u as MXFP4 rows (W4A4).
+template <bool Q>
 __global__ __launch_bounds__(256) void k_prenorm(const uint16_t* __restrict__ x,
-                                                 uint16_t* __restrict__ u, int H, float eps) {
+                                                 uint16_t* __restrict__ u, int H, float eps,
+                                                 uint8_t* __restrict__ uq) {
   __shared__ double red[4];
   const int t = blockIdx.x;
   uint4 v[2];
@@ -819,7 +866,22 @@ __global__ __launch_bounds__(256) void k_prenorm(const uint16_t* __restrict__ x,
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int k8 = threadIdx.x + 256 * i;
-    if (k8 < H / 8) *(uint4*)(u + (size_t)t * H + 8 * k8) = scale8(v[i], rs);
+    const uint4 uv = scale8(v[i], rs);
+    if (k8 < H / 8) *(uint4*)(u + (size_t)t * H + 8 * k8) = uv;
+    if constexpr (Q) mxfp4_store8(uv, k8, uq + (size_t)t * mxfp4_row_bytes(H), H, k8 < H / 8);
+  }
+}
+
+// x as MXFP4 rows (W4A4 without a pre-norm), so that gate/up stages them as
+// they are: one workgroup per token, H <= 4096.
+__global__ __launch_bounds__(256) void k_quant_x(const uint16_t* __restrict__ x, int H,
+                                                 uint8_t* __restrict__ xq) {
+  const int t = blockIdx.x;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int k8 = threadIdx.x + 256 * i;
+    const uint4 v = k8 < H / 8 ? ldg16(x + (size_t)t * H + 8 * k8) : make_uint4(0u, 0u, 0u, 0u);
+    mxfp4_store8(v, k8, xq + (size_t)t * mxfp4_row_bytes(H), H, k8 < H / 8);
   }
 }
 
@@ -890,7 +952,9 @@ hipError_t launch_batched_fmt(const BatchedArgs& a, hipStream_t s) {
   hipError_t err = launch_gemm<FMT, 0, A4>(a, s);
   if (err != hipSuccess) return err;
   if ((err = launch_gemm<FMT, 1, A4>(a, s)) != hipSuccess) return err;
-  return launch_combine(a.ybuf, a.rw, a.residual, a.out, a.T, a.K, a.H, s, a.unext, a.eps);
+  // under W4A4 the next layer's pre-norm is also written quantised
+  return launch_combine(a.ybuf, a.rw, a.residual, a.out, a.T, a.K, a.H, s, a.unext, a.eps,
+                        A4 && a.unext ? a.xqbuf : nullptr);
 }
 
 }  // namespace
@@ -908,21 +972,28 @@ hipError_t launch_sort(const int32_t* ids, int npairs, int E, int32_t* counts, i
 
 hipError_t launch_combine(const uint16_t* y, const uint16_t* rw, const uint16_t* residual,
                           uint16_t* out, int T, int K, int H, hipStream_t s, uint16_t* u,
-                          float eps) {
+                          float eps, uint8_t* uq) {
   if (T == 0) return hipSuccess;
   dim3 grid((H / 8 + 255) / 256, T);
   if (u && H <= 2048)
-    return launch_kernel(MOE_KERNEL_COMBINE, k_combine<true>, grid, dim3(256), 0, s, y, rw,
-                         residual, out, K, H, u, eps);
-  hipError_t e = launch_kernel(MOE_KERNEL_COMBINE, k_combine<false>, grid, dim3(256), 0, s, y, rw,
-                               residual, out, K, H, (uint16_t*)nullptr, eps);
+    return uq ? launch_kernel(MOE_KERNEL_COMBINE, k_combine<true, true>, grid, dim3(256), 0, s, y,
+                              rw, residual, out, K, H, u, eps, uq)
+              : launch_kernel(MOE_KERNEL_COMBINE, k_combine<true, false>, grid, dim3(256), 0, s, y,
+                              rw, residual, out, K, H, u, eps, (uint8_t*)nullptr);
+  hipError_t e = launch_kernel(MOE_KERNEL_COMBINE, k_combine<false, false>, grid, dim3(256), 0, s,
+                               y, rw, residual, out, K, H, (uint16_t*)nullptr, eps,
+                               (uint8_t*)nullptr);
   if (e != hipSuccess || !u) return e;
-  return launch_prenorm(out, u, T, H, eps, s);
+  return launch_prenorm(out, u, T, H, eps, s, uq);
 }
 
-hipError_t launch_prenorm(const uint16_t* x, uint16_t* u, int T, int H, float eps, hipStream_t s) {
+hipError_t launch_prenorm(const uint16_t* x, uint16_t* u, int T, int H, float eps, hipStream_t s,
+                          uint8_t* uq) {
   if (T == 0) return hipSuccess;
-  return launch_kernel(MOE_KERNEL_PRENORM, k_prenorm, dim3(T), dim3(256), 0, s, x, u, H, eps);
+  return uq ? launch_kernel(MOE_KERNEL_PRENORM, k_prenorm<true>, dim3(T), dim3(256), 0, s, x, u, H,
+                            eps, uq)
+            : launch_kernel(MOE_KERNEL_PRENORM, k_prenorm<false>, dim3(T), dim3(256), 0, s, x, u,
+                            H, eps, (uint8_t*)nullptr);
 }
 
 hipError_t launch_batched(const BatchedArgs& a0, int fmt, hipStream_t s) {
@@ -930,13 +1001,26 @@ hipError_t launch_batched(const BatchedArgs& a0, int fmt, hipStream_t s) {
   // the pre-norm once per call (or already done by the previous layer's
   // combine), not once per workgroup and item inside the GEMM
   BatchedArgs a = a0;
+  // W4A4: x is quantised once per call -- by the pre-norm (in the stack the
+  // previous layer's combine has done both) or, without one, by k_quant_x --
+  // and gate/up stages the MXFP4 rows as they are; with the debug dump of u
+  // gate/up quantises its rows itself
+  const bool a4 = (a.flags & MOE_FLAG_W4A4) != 0;
+  a.xq = nullptr;
   if (a.flags & MOE_FLAG_PRENORM) {
     if (!a.x_normed) {
-      const hipError_t e = launch_prenorm(a.x, a.ubuf, a.T, a.H, a.eps, s);
+      const hipError_t e = launch_prenorm(a.x, a.ubuf, a.T, a.H, a.eps, s,
+                                          a4 && !a.du ? a.xqbuf : nullptr);
       if (e != hipSuccess) return e;
     }
     a.x = a.ubuf;
+    if (a4 && !a.du) a.xq = a.xqbuf;
     a.flags &= ~MOE_FLAG_PRENORM;
+  } else if (a4 && !a.du) {
+    const hipError_t e = launch_kernel(MOE_KERNEL_QUANT_X, k_quant_x, dim3(a.T), dim3(256), 0, s,
+                                       a.x, a.H, a.xqbuf);
+    if (e != hipSuccess) return e;
+    a.xq = a.xqbuf;
   }
   if (a.flags & MOE_FLAG_W4A4)  // the API admits it with E8M0 scales only
     return fmt == MOE_SCALE_E8M0_G32 ? launch_batched_fmt<MOE_SCALE_E8M0_G32, true>(a, s)

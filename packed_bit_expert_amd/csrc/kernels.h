@@ -56,7 +56,9 @@ struct BatchedArgs {
   int* err;
   uint16_t* ubuf;     // [T][H] the pre-normed input (MOE_FLAG_PRENORM)
   uint16_t* unext;    // [T][H] or null: where the combine writes the pre-norm of out
-  bool x_normed;      // ubuf already holds the pre-norm of x
+  uint8_t* xqbuf;     // [T][mxfp4_row_bytes(H)]: the pre-norm as MXFP4 rows (W4A4)
+  const uint8_t* xq;  // set by the launcher: xqbuf when it holds this call's rows, else null
+  bool x_normed;      // ubuf already holds the pre-norm of x (and xqbuf its MXFP4 rows under W4A4)
   int ncu;            // CUs of the device (set by the launcher)
   int T, H, I, K, E;
   uint32_t flags;
@@ -76,11 +78,13 @@ hipError_t launch_batched(const BatchedArgs& a, int fmt, hipStream_t s);
 hipError_t launch_sort(const int32_t* ids, int npairs, int E, int32_t* counts, int32_t* offsets,
                        int32_t* perm, int32_t* active, int32_t* nactive, int* err, uint32_t flags,
                        hipStream_t s);
-// With u (not null) the combine also writes u = the pre-norm of out.
+// With u (not null) the combine also writes u = the pre-norm of out, and with
+// uq (not null) u as MXFP4 rows as well.
 hipError_t launch_combine(const uint16_t* y, const uint16_t* rw, const uint16_t* residual,
                           uint16_t* out, int T, int K, int H, hipStream_t s,
-                          uint16_t* u = nullptr, float eps = 0.f);
-hipError_t launch_prenorm(const uint16_t* x, uint16_t* u, int T, int H, float eps, hipStream_t s);
+                          uint16_t* u = nullptr, float eps = 0.f, uint8_t* uq = nullptr);
+hipError_t launch_prenorm(const uint16_t* x, uint16_t* u, int T, int H, float eps, hipStream_t s,
+                          uint8_t* uq = nullptr);
 hipError_t launch_dequant(const uint8_t* nib, const uint8_t* sc, int rows, int cols, int fmt,
                           uint16_t* out, hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);

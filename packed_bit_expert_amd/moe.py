@@ -66,7 +66,8 @@ class Cfg(C.Structure):
 KERNEL_KINDS = {1: "decode gate/up", 2: "decode down + combine", 3: "slot resolve",
                 4: "batched gate/up GEMM", 5: "batched down GEMM", 6: "combine", 7: "sort",
                 8: "dequant", 9: "stream read", 10: "workspace fill", 11: "delay",
-                12: "router", 13: "pre-norm"}
+                12: "router", 13: "pre-norm",
+                14: "x to MXFP4"}
 
 
 class Dump(C.Structure):

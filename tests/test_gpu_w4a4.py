@@ -126,3 +126,67 @@ def test_w4a4_stack_matches_chain_and_oracle():
         GH.compare(got, nxt, f"w4a4 stack layer{l}")
         hx = nxt
     del store
+
+
+@pytest.mark.parametrize("workload,prenorm", [("c2", True), ("c3", True), ("c2", False),
+                                              ("c3", False)])
+def test_w4a4_x_quantised_once(layer_mx, workload, prenorm):
+    """u is quantised to MXFP4 rows once per call -- by the pre-norm kernel,
+    or without one by a quantising kernel -- and gate/up stages the rows as
+    they are; the debug call quantises u inside gate/up instead.  The two
+    quantise the same BF16 values with the same rule, so the outputs must
+    agree bit for bit, and both match the oracle."""
+    w = S.WORKLOADS[workload]
+    banner(f"W4A4 {workload} T={w.tokens} u quantised once, prenorm={prenorm}")
+    x, ids, rw = S.inputs(w, 0, 1)
+    r = S.activations(8, 0, 1, x.shape[0], LFM.hidden)
+    flags = M.FLAG_W4A4 | (M.FLAG_PRENORM if prenorm else 0)
+    got, st = layer_mx.gpu(x, ids, rw, residual=r, flags=flags)
+    assert st == 0
+    dbg, _, st = layer_mx.gpu(x, ids, rw, residual=r, flags=flags, dumps=True)
+    assert st == 0
+    assert np.array_equal(got, dbg), "fused quantisation == in-GEMM quantisation"
+    ref = layer_mx.oracle(x, ids, rw, residual=r, prenorm=prenorm, w4a4=True)
+    GH.compare(got, ref, f"w4a4 {workload} prenorm={prenorm}")
+
+
+def test_w4a4_wide_stack_matches_chain():
+    """H = 4096: the combine cannot finish a row's pre-norm in one workgroup,
+    so a pre-norm launch after it writes the next layer's u and its MXFP4
+    rows.  The stack equals the chained single-layer calls bit for bit and
+    its first layer matches the oracle."""
+    sh = S.Shape(hidden=4096, inter=512, experts=8, top_k=2, layers=3)
+    T, L = 6, sh.layers
+    banner(f"W4A4 stack of {L} layers at H={sh.hidden} I={sh.inter}, T={T}")
+    store = ResidentExperts(sh, S.FMT_E8M0_G32, L).fill_synthetic()
+    x = S.activations(5, 0, 0, T, sh.hidden)
+    routes = [S.routing_uniform(5, l, 0, T, sh.experts, sh.top_k) for l in range(L)]
+    ids = np.stack([r[0] for r in routes])
+    rw = np.stack([r[1] for r in routes])
+    out = torch.empty((T, sh.hidden), dtype=torch.bfloat16, device=GH.dev())
+    cfg = M.make_cfg(T, sh.hidden, sh.inter, sh.experts, sh.top_k, flags=M.FLAG_W4A4,
+                     prenorm_eps=GH.EPS)
+    ws = torch.zeros(M.moe_w4a16_workspace_bytes(cfg), dtype=torch.uint8, device=GH.dev())
+    cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), ws.numel()
+    M.moe_w4a16_stack_forward(L, GH.bf16_dev(x), GH.i32_dev(ids), GH.bf16_dev(rw), store.wtab,
+                              store.stab, None, out, cfg)
+    torch.cuda.synchronize()
+    stack = GH.bits_host(out)
+    h = GH.bf16_dev(x)
+    for l in range(L):
+        wt, stb, _ = store.layer_tables(l)
+        o = torch.empty_like(h)
+        c = M.make_cfg(T, sh.hidden, sh.inter, sh.experts, sh.top_k,
+                       flags=M.FLAG_PRENORM | M.FLAG_W4A4, residual=h, prenorm_eps=GH.EPS)
+        wsl = torch.zeros(M.moe_w4a16_workspace_bytes(c), dtype=torch.uint8, device=GH.dev())
+        c.workspace, c.workspace_bytes = wsl.data_ptr(), wsl.numel()
+        M.moe_w4a16_forward(h, GH.i32_dev(ids[l]), GH.bf16_dev(rw[l]), wt, stb, o, c)
+        h = o
+    torch.cuda.synchronize()
+    assert np.array_equal(stack, GH.bits_host(h))
+    lay = GH.Layer(sh, S.FMT_E8M0_G32, 0, store=store, l=0)
+    ref = lay.oracle(x, ids[0], rw[0], residual=x, prenorm=True, w4a4=True)
+    got, st = lay.gpu(x, ids[0], rw[0], residual=x, flags=M.FLAG_PRENORM | M.FLAG_W4A4)
+    assert st == 0
+    GH.compare(got, ref, "w4a4 wide layer 0")
+    del store
