@@ -9,7 +9,8 @@
 //      MXFP4 card); k_sort is the same grouping as a stand-alone hook;
 //   2. with MOE_FLAG_PRENORM, k_prenorm: the weightless RMS pre-norm of x,
 //      once per call (in the layer stack the previous layer's combine has
-//      already written it);
+//      already written it); under MOE_FLAG_W4A4 it also writes x as MXFP4
+//      rows (k_quant_x does that alone without a pre-norm);
 //   3. k_bat_gemm<MODE 0>: persistent workgroups walk (expert pass, 64-row
 //      tile) work: the pass's token rows are staged in LDS, packed gate and up
 //      rows are dequantised to BF16 MFMA operands in registers (exact, no
@@ -17,7 +18,7 @@
 //      the epilogue writes h = bf16(silu(bf16 g) * bf16 u) per pair;
 //   4. k_bat_gemm<MODE 1>: the same for down, writing y per (token, slot);
 //   5. k_combine: the slot-order BF16 combine per token (+ residual, and in
-//      the stack the next layer's pre-norm).
+//      the stack the next layer's pre-norm, under W4A4 also as MXFP4 rows).
 // At these sizes the work is still HBM-bound (12-15 flop per weight byte
 // against a BF16-MFMA ridge near 312): MFMA removes the multiply-adds from
 // the VALU, which is left with the dequantisation.
@@ -393,9 +394,10 @@ __device__ void collect_pairs(const int32_t* ids, int id0, int npairs, int e, in
 
 // Stage the 16 A rows of a pass into LDS with the gfx950 direct global->LDS
 // load: one wave instruction moves 1 KiB (16 bytes per lane, lane i at
-// base + 16 i).  A row is Kd BF16 values (x or h), or, for down under W4A4,
-// the MXFP4 row of h that gate/up wrote (mxfp4_row_bytes(Kd) bytes).  Rows
-// past the pass's pair count are zero-filled with ordinary LDS stores.
+// base + 16 i).  A row is Kd BF16 values (x or h), or under W4A4 an MXFP4 row
+// (mxfp4_row_bytes(Kd) bytes): h as gate/up wrote it, and x as the pre-norm or
+// k_quant_x wrote it.  Rows past the pass's pair count are zero-filled with
+// ordinary LDS stores.
 template <int MODE, bool A4>
 __device__ __forceinline__ void stage_rows(const BatchedArgs& a, const int* lp, int mcnt, int Kd,
                                            int ldx, uint16_t* xs, int wave, int lane) {
@@ -620,7 +622,7 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
       }
     }
     if constexpr (A4 && MODE == 0) {  // down's rows of h arrive quantised
-      if (!a.xq) {                     // and so do x's when the pre-norm quantised them
+      if (!a.xq) {  // x's too, except in the debug call, which dumps u from these rows
         quant_rows_mxfp4(xs, ldx, Kd, it.mcnt, wave, lane);
         lds_barrier();
       }

@@ -2,8 +2,9 @@
 
 "primitive-ai/LFM2.5-24B-A2B-NVFP4A16", "Why this quant": the W4A4 builds make
 the expert activations 4-bit as well and run on FP4 matrix hardware.  Here u
-and every h are quantised to MXFP4 in LDS and multiplied on the gfx950
-block-scaled FP4 MFMA.  Quantised codes are integer decisions taken from the
+and every h are quantised to MXFP4 once (u where the pre-norm or a quantising
+kernel writes it, h in the gate/up epilogue; the debug call quantises the
+staged u rows in LDS) and multiplied on the gfx950 block-scaled FP4 MFMA.  Quantised codes are integer decisions taken from the
 same BF16 inputs on both sides, so the dumps (g, v, h, y) are expected to be
 bit-identical almost everywhere; the bound is the tolerance of gpu_helpers.
 """
