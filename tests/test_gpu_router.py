@@ -121,7 +121,7 @@ def routed_stack():
     torch.cuda.empty_cache()
 
 
-def _routed_single(st, wrd, bd, x, L, T):
+def _routed_single(st, wrd, bd, x, L, T, flags=0):
     """The routed stack as L single-layer routed calls (pre-norm + residual)."""
     h = GH.bf16_dev(x)
     ids_all, outs = [], []
@@ -130,7 +130,7 @@ def _routed_single(st, wrd, bd, x, L, T):
         out = torch.empty_like(h)
         ids = torch.empty((T, 4), dtype=torch.int32, device=GH.dev())
         rw = torch.empty((T, 4), dtype=torch.bfloat16, device=GH.dev())
-        cfg = M.make_cfg(T, flags=M.FLAG_PRENORM, residual=h, prenorm_eps=GH.EPS)
+        cfg = M.make_cfg(T, flags=M.FLAG_PRENORM | flags, residual=h, prenorm_eps=GH.EPS)
         ws = torch.zeros(M.moe_w4a16_workspace_bytes(cfg), dtype=torch.uint8, device=GH.dev())
         cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), ws.numel()
         M.moe_w4a16_forward_routed(h, wrd[l], bd[l], wt, stb, out, ids, rw, cfg)
@@ -141,11 +141,11 @@ def _routed_single(st, wrd, bd, x, L, T):
     return GH.bits_host(outs[-1]), np.stack([i.cpu().numpy() for i in ids_all])
 
 
-def _routed_stack(st, wrd, bd, x, L, T):
+def _routed_stack(st, wrd, bd, x, L, T, flags=0):
     out = torch.empty((T, LFM.hidden), dtype=torch.bfloat16, device=GH.dev())
     ids = torch.empty((L, T, 4), dtype=torch.int32, device=GH.dev())
     rw = torch.empty((L, T, 4), dtype=torch.bfloat16, device=GH.dev())
-    cfg = M.make_cfg(T, prenorm_eps=GH.EPS)
+    cfg = M.make_cfg(T, flags=flags, prenorm_eps=GH.EPS)
     ws = torch.zeros(M.moe_w4a16_workspace_bytes(cfg), dtype=torch.uint8, device=GH.dev())
     cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), ws.numel()
     M.moe_w4a16_stack_forward_routed(L, GH.bf16_dev(x), wrd, bd, st.wtab, st.stab, None, out, ids,
@@ -187,6 +187,28 @@ def test_routed_stack(routed_stack, T):
         if np.array_equal(gid.cpu().numpy(), rids):
             GH.compare(GH.bits_host(gl), nxt, f"routed layer {l}")
         h = nxt
+
+
+def test_routed_stack_w4a4(routed_stack):
+    """Routed stack under W4A4 (T = 32, 8 layers): each layer's combine also
+    writes the next layer's pre-normed input as MXFP4 rows, which the next
+    layer's gate/up stages as they are (its router reads the layer input).
+    The stack equals 8 single-layer routed W4A4 calls bit for bit, and the
+    first layer matches the oracle's routing and W4A4 layer."""
+    st, wr, b, wrd, bd = routed_stack
+    L, T = 8, 32
+    banner(f"routed W4A4 stack L={L} T={T}")
+    x = S.activations(FAMILY, 0, 9, T, LFM.hidden)
+    got, ids = _routed_stack(st, wrd, bd, x, L, T, flags=M.FLAG_W4A4)
+    chain, ids_c = _routed_single(st, wrd, bd, x, L, T, flags=M.FLAG_W4A4)
+    assert np.array_equal(got, chain) and np.array_equal(ids, ids_c)
+    rids, rrw, lg = O.route(x, wr[0], b[0], top_k=4, prenorm=True, eps=GH.EPS, logits=True)
+    check_ids(ids[0], rids, lg, b[0], 4)
+    if np.array_equal(ids[0], rids):
+        lay = GH.Layer(LFM, S.FMT_E8M0_G32, 0, store=st, l=0)
+        ref = lay.oracle(x, rids, rrw, residual=x, prenorm=True, w4a4=True)
+        g1, _ = _routed_single(st, wrd, bd, x, 1, T, flags=M.FLAG_W4A4)
+        GH.compare(g1, ref, "routed w4a4 layer 0")
 
 
 def test_routed_stack_graph_replay(routed_stack):
