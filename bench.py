@@ -37,6 +37,10 @@ def parse():
                    choices=["c1", "c0", "c2", "c2stack", "c3", "c4", "c4b32", "c1serial",
                             "c1routed", "c2w4a4", "c3w4a4", "c2stackw4a4", "c1hybrid"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-batch32", action="store_true",
+                   help="skip the concurrency-32 sub-record of the default (c1) run")
+    p.add_argument("--batch32-steps", type=int, default=64,
+                   help="timed layer calls of the concurrency-32 sub-record")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--calib", action="store_true",
                    help="also run a 1 GiB stream read and a 256 MiB copy (counter calibration)")
@@ -60,10 +64,8 @@ def main():
               "(expert-parallel sharding is a design note, not code). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    from packed_bit_expert_amd import moe as M
     from packed_bit_expert_amd import synth as S
     from packed_bit_expert_amd.residency import ResidentExperts
 
@@ -73,23 +75,111 @@ def main():
         run_hybrid(args, dev)
         return
     shape = S.LFM24B
-    wname = {"c2stack": "c2", "c1serial": "c1", "c1routed": "c1", "c2w4a4": "c2", "c3w4a4": "c3",
-             "c2stackw4a4": "c2"}.get(args.workload, args.workload)
-    routed = args.workload == "c1routed"
-    w4a4 = args.workload.endswith("w4a4")
-    w = S.WORKLOADS[wname]
-    stack = args.workload in ("c1", "c2stack", "c1serial", "c1routed", "c2stackw4a4")
-    T, E, K, H = w.tokens, shape.experts, shape.top_k, shape.hidden
+    w = S.WORKLOADS[base_workload(args.workload)]
     # layers resident: the whole 38-layer stack for every workload, so single-
     # layer workloads rotate over 38 layers and the reuse distance (762 MB+ per
     # token) exceeds the 256 MB Infinity Cache.
     L = shape.layers
     t0 = time.time()
     store = ResidentExperts(shape, w.fmt, L, device=dev).fill_synthetic()
-    print(f"[bench] {L} layers x {E} experts resident ({store.buf.numel() / 1e9:.2f} GB) "
+    print(f"[bench] {L} layers x {shape.experts} experts resident ({store.buf.numel() / 1e9:.2f} GB) "
           f"in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    stream = torch.cuda.Stream()  # capture needs a non-default stream; every launch and event uses it
+    torch.cuda.set_stream(stream)
+    res = measure(args, args.workload, store, stream, dev, args.steps, args.warmup,
+                  args.cpu_seconds)
+    # The metric is quoted at batch 1 and at batch 32: the default run adds the
+    # concurrency-32 workload (T = 32, Zipf(1.1) routing, one layer per call
+    # rotating over the 38 resident layers, graph replay) as a sub-record with
+    # its own roofline, MFMA use and oracle baseline.
+    if args.workload == "c1" and not args.no_batch32:
+        sub = measure(args, "c2", store, stream, dev, args.batch32_steps, max(16, args.warmup),
+                      args.cpu_seconds * 2 / 3, calib=False)
+        res["batch32"] = {k: sub[k] for k in ("metric", "value", "unit", "ms_per_step", "steps",
+                                                 "warmup", "dtype", "config", "roofline",
+                                                 "kernels", "cpu_baseline")}
+        res["batch32"]["ms_per_call"] = sub["ms_per_step"]
+    print(json.dumps(res), flush=True)
 
-    nsteps = args.warmup + args.steps
+
+def decode_floor(args, store, stream, dev, xs, ids, rws, cfg, warmup, steps, buf, sink):
+    """What the batch-1 decode kernels cost without their arithmetic, each
+    figure event-timed like the kernels themselves (the library's
+    per-dispatch events, launches queued behind a delay kernel):
+      loads_only_us   the stack's launches with each layer's two decode
+                      kernels replaced by kernels of the same grid that read
+                      the same bytes in the same order after the same
+                      dependent slot load, with no arithmetic (per kind: 1 =
+                      gate/up, 2 = down);
+      empty_us        an empty kernel with each decode kernel's grid;
+      burst_read_us   a read of each kernel's algorithmic byte count in which
+                      every lane issues all of its 16-byte loads before using
+                      any (1, 2, 4 or 8 per lane), each launch at a new
+                      offset of a 1 GiB buffer."""
+    import numpy as np
+
+    from packed_bit_expert_amd import moe as M
+    L = store.layers
+    nt = min(args.timing_steps, steps)
+    durs = {}
+    for c0 in range(0, nt, 4):
+        M.moe_w4a16_delay(30000, stream)
+        M.moe_w4a16_timing_begin(1024)
+        for s in range(warmup + c0, warmup + min(nt, c0 + 4)):
+            M.moe_w4a16_decode_floor(L, xs[s], ids[s], rws[s], store.wtab, store.stab, sink, cfg)
+        msl, kinds = M.moe_w4a16_timing_end(1024)
+        for d, k in zip(msl, kinds):
+            durs.setdefault(k, []).append(d)
+    loads_only = {"1": float(np.mean(durs[15]) * 1e3), "2": float(np.mean(durs[16]) * 1e3)}
+
+    def timed(launch, n=128):
+        ts = []
+        for c0 in range(0, n, 64):
+            M.moe_w4a16_delay(30000, stream)
+            M.moe_w4a16_timing_begin(64)
+            for i in range(c0, c0 + 64):
+                launch(i)
+            msl, _ = M.moe_w4a16_timing_end(64)
+            ts += msl
+        return float(np.mean(ts) * 1e3)
+
+    empty = {"1": timed(lambda i: M.moe_w4a16_empty_launch(768, 256, sink, stream)),
+             "2": timed(lambda i: M.moe_w4a16_empty_launch(256, 256, sink, stream))}
+    burst = {}
+    for kind, nb in (("1", 13373440), ("2", 6692864)):
+        nreg = buf.numel() // nb
+        burst[kind] = {str(lpl): timed(lambda i, lpl=lpl: M.moe_w4a16_read_burst(
+            buf.data_ptr() + (i % nreg) * nb, nb, lpl, sink, stream)) for lpl in (1, 2, 4, 8)}
+    return {"loads_only_us": loads_only, "empty_us": empty, "burst_read_us": burst,
+            "burst_read_best_us": {k: min(v.values()) for k, v in burst.items()},
+            "note": "kinds: 1 = decode gate/up (13,373,440 B per launch), 2 = decode down + "
+                    "combine (6,692,864 B per launch)"}
+
+
+def base_workload(k):
+    """The synthetic input family (synth.WORKLOADS key) of a bench workload."""
+    return {"c2stack": "c2", "c1serial": "c1", "c1routed": "c1", "c2w4a4": "c2", "c3w4a4": "c3",
+            "c2stackw4a4": "c2", "c1floor": "c1"}.get(k, k)
+
+
+def measure(args, wkey, store, stream, dev, steps, warmup, cpu_seconds, calib=None):
+    """Time `steps` steps of workload `wkey` (after `warmup` untimed ones) on
+    the resident experts, then the per-kernel durations, the read ceilings and
+    the oracle baseline; returns the result record."""
+    import numpy as np
+    import torch
+
+    from packed_bit_expert_amd import moe as M
+    from packed_bit_expert_amd import synth as S
+
+    shape = S.LFM24B
+    routed = wkey == "c1routed"
+    w4a4 = wkey.endswith("w4a4")
+    w = S.WORKLOADS[base_workload(wkey)]
+    stack = wkey in ("c1", "c2stack", "c1serial", "c1routed", "c2stackw4a4")
+    T, E, K, H = w.tokens, shape.experts, shape.top_k, shape.hidden
+    L = shape.layers
+    nsteps = warmup + steps
     # per-step inputs (resident before timing)
     if stack:
         xs = torch.stack([torch.from_numpy(S.activations(w.family, 0, s, T, H).view(np.int16))
@@ -113,9 +203,7 @@ def main():
                                         for l in range(L)])).view(torch.bfloat16).to(dev)
         rbias = torch.from_numpy(np.stack([S.expert_bias(shape, w.family, l)
                                            for l in range(L)])).to(dev)
-    stream = torch.cuda.Stream()  # capture needs a non-default stream; every launch and event uses it
-    torch.cuda.set_stream(stream)
-    flags = M.FLAG_SERIAL if args.workload == "c1serial" else 0
+    flags = M.FLAG_SERIAL if wkey == "c1serial" else 0
     if w4a4:
         flags |= M.FLAG_W4A4
     cfg = M.make_cfg(T, H, shape.inter, E, K, w.fmt, prenorm_eps=EPS, stream=stream, flags=flags)
@@ -138,7 +226,7 @@ def main():
                 cfg.tensor_scales = store.tscales[l].data_ptr()
             M.moe_w4a16_forward(xs[s], ids[s], rws[s], store.wtab[l], store.stab[l], out[s], cfg)
 
-    for s in range(args.warmup):
+    for s in range(warmup):
         step(s)
     torch.cuda.synchronize()
 
@@ -146,7 +234,7 @@ def main():
     if not args.eager:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
-            for s in range(args.warmup, nsteps):
+            for s in range(warmup, nsteps):
                 step(s)
         torch.cuda.synchronize()
 
@@ -156,23 +244,25 @@ def main():
     if graph is not None:
         graph.replay()
     else:
-        for s in range(args.warmup, nsteps):
+        for s in range(warmup, nsteps):
             step(s)
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1)
-    ms_step = ms / args.steps
+    ms_step = ms / steps
+    print(f"[bench] {wkey}: {steps} steps in {ms:.3f} ms ({ms_step:.4f} ms per step)",
+          file=sys.stderr, flush=True)
 
     # algorithmic bytes: each call reads its distinct selected experts' packed
     # bytes once, plus activations in and out
-    ids_h = ids[args.warmup:].cpu().numpy()
+    ids_h = ids[warmup:].cpu().numpy()
     if stack:
-        distinct = [len(np.unique(ids_h[s, l])) for s in range(args.steps) for l in range(L)]
+        distinct = [len(np.unique(ids_h[s, l])) for s in range(steps) for l in range(L)]
     else:
-        distinct = [len(np.unique(ids_h[s])) for s in range(args.steps)]
+        distinct = [len(np.unique(ids_h[s])) for s in range(steps)]
     layer_calls = len(distinct)
     act = T * H * 2
-    if args.workload == "c1serial":
+    if wkey == "c1serial":
         per_kind = kernel_bytes_serial(shape, w, T)
     else:
         per_kind = kernel_bytes(shape, w, T, float(np.mean(distinct)), chained=w.chained)
@@ -187,14 +277,14 @@ def main():
     kernels = []
     dominant = None
     if args.timing_steps > 0:
-        nt = min(args.timing_steps, args.steps)
+        nt = min(args.timing_steps, steps)
         chunk = 4 if stack else 64
         cap = 4096
         durs = {}
         for c0 in range(0, nt, chunk):
             M.moe_w4a16_delay(30000, stream)
             M.moe_w4a16_timing_begin(cap)
-            for s in range(args.warmup + c0, args.warmup + min(nt, c0 + chunk)):
+            for s in range(warmup + c0, warmup + min(nt, c0 + chunk)):
                 step(s)
             msl, kinds = M.moe_w4a16_timing_end(cap)
             for d, k in zip(msl, kinds):
@@ -247,7 +337,13 @@ def main():
             ts += msl
         torch.cuda.synchronize()
         plain_us = float(np.mean(ts) * 1e3)
-    if args.calib:
+    # the decode path's floor: the same launches with no arithmetic, empty
+    # launches of the same grids, and reads of the same byte counts in which
+    # every lane issues all of its loads up front
+    floor = None
+    if wkey == "c1" and args.timing_steps > 0:
+        floor = decode_floor(args, store, stream, dev, xs, ids, rws, cfg, warmup, steps, buf, sink)
+    if args.calib if calib is None else calib:
         # counter calibration: one more 1 GiB read and a 256 MiB device copy
         M.moe_w4a16_stream_read(buf, buf.numel(), sink, stream)
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -258,19 +354,24 @@ def main():
 
     cpu = cpu1 = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, shape, args.cpu_seconds, w4a4=w4a4)
+        cpu = cpu_baseline(w, shape, cpu_seconds, w4a4=w4a4)
         # the same oracle on one thread, over a shorter sample
-        cpu1 = cpu_baseline(w, shape, args.cpu_seconds / 2, w4a4=w4a4, nthreads=1)
+        cpu1 = cpu_baseline(w, shape, cpu_seconds / 2, w4a4=w4a4, nthreads=1)
 
     if dominant is not None and "achieved_GBps" in dominant:
         roof = {"bound": "hbm", "achieved": dominant["achieved_GBps"], "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": dominant["achieved_GBps"] / HBM_PEAK_GBPS,
-                "traffic": traffic_for(dominant["_kind"], args.workload),
+                "traffic": traffic_for(dominant["_kind"], base_workload(wkey)),
                 "kernel": dominant["kernel"],
                 "alg_bytes_per_launch": dominant["alg_bytes_per_launch"],
                 "mean_launch_us": dominant["mean_us"],
                 "plain_read_same_bytes_us": plain_us,
                 "frac_of_plain_read": plain_us / dominant["mean_us"] if plain_us else None}
+        if floor is not None and dominant["_kind"] in (1, 2):
+            lo = floor["loads_only_us"][str(dominant["_kind"])]
+            roof["floor"] = floor
+            roof["floor_us"] = lo
+            roof["frac_of_floor"] = lo / dominant["mean_us"]
         if dominant["_kind"] in (4, 5):
             fl = kernel_flops(shape, T, dominant["_kind"])
             roof["mfma_useful_TFLOPs"] = fl / (dominant["mean_us"] / 1e6) / 1e12
@@ -285,13 +386,13 @@ def main():
         r.pop("_kind")
         r.pop("_total")
 
-    res = {
+    return {
         "metric": "MoE-layer tokens/s & achieved HBM GB/s (% of peak), 24B-A2B shape, batch 1/32",
         "value": tok_layer_per_s,
         "unit": "tokens/s per MoE layer",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -299,15 +400,16 @@ def main():
         "dtype": "fp4" if w4a4 else "bf16",
         "data": "synthetic (seeded E2M1 nibbles, E8M0 117..123 or E4M3 normal scales, x ~ N(0,1) BF16)",
         "config": {
-            "workload": workload_name(args.workload),
+            "workload": workload_name(wkey),
             "hidden": H, "inter": shape.inter, "experts": E, "top_k": K,
             "layers_per_step": L if stack else 1, "tokens_per_step": T,
             "weights": "E2M1 + E4M3/16 + FP32 tensor scale" if w.fmt else "E2M1 + E8M0/32",
-            "stack_tokens_per_s": T * args.steps / secs if stack else None,
+            "stack_tokens_per_s": T * steps / secs if stack else None,
             "graph_replay": not args.eager,
             "step_achieved_GBps": achieved_step,
             "step_frac_of_peak": achieved_step / HBM_PEAK_GBPS,
-            "algorithmic_bytes_per_step": alg_bytes / args.steps,
+            "algorithmic_bytes_per_step": alg_bytes / steps,
+            "mean_distinct_experts_per_layer_call": float(np.mean(distinct)),
         },
         "roofline": roof,
         "kernels": kernels,
@@ -315,7 +417,6 @@ def main():
         "cpu_baseline": cpu,
         "cpu_baseline_1thread": cpu1,
     }
-    print(json.dumps(res), flush=True)
 
 
 def run_hybrid(args, dev):
@@ -584,6 +685,19 @@ def workload_name(k):
     }[k]
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or None
+
+
 def cpu_baseline(w, shape, target_s, w4a4=False, nthreads=0):
     """The oracle as it stands on this host's cores (all of them, or
     `nthreads`), on a bounded sample of the workload: layer calls of the
@@ -623,7 +737,7 @@ def cpu_baseline(w, shape, target_s, w4a4=False, nthreads=0):
             h = out
         calls += 1
     return {"value": T * calls / busy, "unit": "tokens/s per MoE layer", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), "host_cpus_online": os.cpu_count(),
             "sample": f"{calls} {'W4A4 ' if w4a4 else ''}layer calls of {T} token(s) on {w.name} inputs (layers 0..{min(calls, shape.layers) - 1}"
                       f"{', chained' if w.chained else ''}), fp64 scalar C oracle with {threads} OpenMP "
                       f"threads, {busy:.1f} s of oracle time (input generation excluded)"}

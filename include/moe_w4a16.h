@@ -15,7 +15,10 @@
  *              from +0; then, with a residual, out = bf16(residual + out).
  *
  * Expert weights stay packed: E2M1 FP4 values two per byte with one E8M0
- * scale per 32 values (MOE_SCALE_E8M0_G32, the MXFP4 card's format), or one
+ * scale per 32 values (MOE_SCALE_E8M0_G32, the MXFP4 card's format; codes
+ * 1..254, i.e. 2^-126 .. 2^127, are supported and decode exactly, including
+ * to BF16 subnormals and infinities; code 0 (2^-127) and the NaN code 255
+ * are outside the supported input range), or one
  * E4M3FN scale per 16 values plus an FP32 per-expert tensor scale shared by
  * gate and up and a second one for down (MOE_SCALE_E4M3_G16, the NVFP4
  * weight-only variant of "primitive-ai/LFM2.5-24B-A2B-NVFP4A16", section
@@ -156,8 +159,11 @@ int moe_w4a16_shape_supported(int32_t hidden, int32_t inter);
 size_t moe_w4a16_workspace_bytes(const moe_w4a16_cfg* cfg);
 
 /* Zero-fill a workspace on `stream` (a kernel, not a memset node, so it can
- * be captured).  A workspace must be zeroed once before its first use; every
- * forward call leaves its control words zeroed again on exit. */
+ * be captured).  A workspace must be zeroed once before its first use.  Its
+ * control words (the device error word and the router's per-token counters)
+ * sit at fixed offsets at its start, whatever the cfg, and every call leaves
+ * the counters at zero again, so one workspace zeroed once may serve calls
+ * of different cfgs (each at least moe_w4a16_workspace_bytes of its cfg). */
 int moe_w4a16_workspace_init(void* workspace, size_t bytes, void* stream);
 
 /*
@@ -295,6 +301,34 @@ int moe_w4a16_device_status(void* workspace, int32_t* host_code, void* stream);
  * bandwidth next to the kernels above. */
 int moe_w4a16_stream_read(const void* src, size_t bytes, void* sink, void* stream);
 
+/*
+ * Measurement helpers for the floor of the batch-1 decode path (what the two
+ * decode kernels of a layer would cost with no arithmetic).
+ *
+ * moe_w4a16_decode_floor: the launch sequence of moe_w4a16_stack_forward at
+ *   T = 1 (same arguments, with `sink` in place of out: device, 16 KiB,
+ *   16-byte aligned) in which each layer's two decode kernels are replaced
+ *   by kernels with the same grid that resolve the same routing slots and
+ *   issue the same loads in the same order -- the selected experts' nibbles
+ *   and scales, x, h, the coefficients and the residual -- and only fold
+ *   them with XOR (no dequantisation, no products, no stores).  Only the
+ *   LFM2.5-24B-A2B shape (hidden 2048, inter 1536, top-4) with E8M0 scales;
+ *   otherwise MOE_ERR_UNSUPPORTED_SHAPE.
+ * moe_w4a16_empty_launch: one kernel of `workgroups` x `threads` (1..1024)
+ *   threads that does nothing (it reads no memory; `sink` is a device word
+ *   it never writes in practice).
+ * moe_w4a16_read_burst: read `bytes` (a multiple of 16) at `src` (16-byte
+ *   aligned) with bytes / (16 * 256 * loads_per_lane) workgroups of 256
+ *   lanes, each lane issuing all of its `loads_per_lane` (1, 2, 4 or 8)
+ *   16-byte loads before it uses any; `sink` as above.
+ */
+int moe_w4a16_decode_floor(int32_t num_layers, const void* x, const int32_t* expert_ids,
+                           const void* route_w, const void* const* packed_weights,
+                           const void* const* scales, void* sink, const moe_w4a16_cfg* cfg);
+int moe_w4a16_empty_launch(int32_t workgroups, int32_t threads, void* sink, void* stream);
+int moe_w4a16_read_burst(const void* src, size_t bytes, int32_t loads_per_lane, void* sink,
+                         void* stream);
+
 /* Measurement helper: one wave that spins for `microseconds` (at most
  * 1,000,000) on the 100 MHz real-time counter, so that a host can enqueue
  * work behind it and the GPU then runs that work back to back. */
@@ -316,6 +350,10 @@ int moe_w4a16_delay(uint32_t microseconds, void* stream);
 #define MOE_KERNEL_PRENORM 13        /* batched: weightless RMS pre-norm of the layer input
                                         (under W4A4 also its MXFP4 rows) */
 #define MOE_KERNEL_QUANT_X 14        /* batched W4A4 without pre-norm: x as MXFP4 rows */
+#define MOE_KERNEL_FLOOR_GATE_UP 15  /* moe_w4a16_decode_floor: decode gate/up's loads only */
+#define MOE_KERNEL_FLOOR_DOWN 16     /* moe_w4a16_decode_floor: decode down's loads only */
+#define MOE_KERNEL_EMPTY 17          /* moe_w4a16_empty_launch */
+#define MOE_KERNEL_READ_BURST 18     /* moe_w4a16_read_burst */
 
 /*
  * Kernel timing (measurement only).  After moe_w4a16_timing_begin(capacity)

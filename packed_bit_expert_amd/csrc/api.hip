@@ -71,7 +71,7 @@ bool capturing(hipStream_t s) {
 constexpr int kStackGroup = 64;  // layers whose routing slots are resolved in one pass
 
 struct Layout {
-  size_t hbuf, hq, ybuf, ping, scratch, ubuf, xq, logits, rcount, slots, total;
+  size_t hbuf, hq, ybuf, ping, scratch, ubuf, xq, logits, slots, total;
 };
 
 Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
@@ -93,8 +93,6 @@ Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K) {
   off += align256((size_t)T * ((H / 2 + H / 32 + 15) & ~(int64_t)15));
   L.logits = off;  // router logits, FP64 [T][E]
   off += align256((size_t)(T * E) * 8);
-  L.rcount = off;  // router: waves done per token (zero between calls)
-  off += align256((size_t)T * 4);
   L.slots = off;
   off += align256((size_t)(T * K) * kStackGroup * sizeof(SlotRef));
   L.total = off;
@@ -395,6 +393,70 @@ int moe_w4a16_stack_forward(int32_t num_layers, const void* x, const int32_t* ex
   return ok();
 }
 
+int moe_w4a16_decode_floor(int32_t num_layers, const void* x, const int32_t* expert_ids,
+                           const void* route_w, const void* const* packed_weights,
+                           const void* const* scales, void* sink, const moe_w4a16_cfg* cfg) {
+  if (num_layers < 1) return fail(MOE_ERR_INVALID_ARG, "num_layers %d < 1", num_layers);
+  if (!cfg) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+  moe_w4a16_cfg lc = *cfg;
+  lc.flags = (lc.flags & ~(uint32_t)MOE_FLAG_PRENORM) | MOE_FLAG_PRENORM;
+  lc.tensor_scales = nullptr;
+  lc.residual = x;
+  Call k{x, expert_ids, route_w, packed_weights, scales, nullptr, x, sink, nullptr};
+  int rc = check_call(&lc, k);
+  if (rc) return rc;
+  if (lc.num_tokens != 1 || lc.scale_fmt != MOE_SCALE_E8M0_G32 ||
+      !decode_floor_supported(lc.hidden, lc.inter, lc.top_k) || (lc.flags & ~(uint32_t)MOE_FLAG_PRENORM))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE,
+                "the decode floor mirrors T = 1, hidden 2048, inter 1536, top-4, E8M0, no flags");
+  const int64_t T = 1, K = lc.top_k, E = lc.num_experts;
+  const Layout L = layout(T, lc.hidden, lc.inter, E, K);
+  uint8_t* ws = (uint8_t*)lc.workspace;
+  SlotRef* slots = (SlotRef*)(ws + L.slots);
+  int* err = &((Ctrl*)ws)->err;
+  hipStream_t s = (hipStream_t)lc.stream;
+  const void* src = x;
+  for (int l = 0; l < num_layers; ++l) {
+    const int g = l % kStackGroup;
+    if (g == 0) {
+      const int nl = num_layers - l < kStackGroup ? num_layers - l : kStackGroup;
+      hipError_t e = launch_resolve(
+          expert_ids + (size_t)l * T * K, (const uint8_t* const*)(packed_weights + (size_t)l * E),
+          (const uint8_t* const*)(scales + (size_t)l * E), nullptr, (int)(nl * T * K), (int)(T * K),
+          (int)E, lc.flags, err, slots, s);
+      if (e != hipSuccess) return hip_fail(e, "slot resolve launch");
+    }
+    // the layer input alternates between x and the workspace's ping buffer,
+    // as in the stack
+    hipError_t e = launch_decode_floor(slots + (size_t)g * T * K, (const uint16_t*)src,
+                                       (uint16_t*)(ws + L.hbuf),
+                                       (const uint16_t*)route_w + (size_t)l * T * K,
+                                       (const uint16_t*)src, (uint32_t*)sink, s);
+    if (e != hipSuccess) return hip_fail(e, "decode floor launch");
+    src = (l % 2 == 0) ? (const void*)(ws + L.ping) : x;
+  }
+  return ok();
+}
+
+int moe_w4a16_empty_launch(int32_t workgroups, int32_t threads, void* sink, void* stream) {
+  if (workgroups < 1 || threads < 1 || threads > 1024 || !sink)
+    return fail(MOE_ERR_INVALID_ARG, "workgroups >= 1, threads 1..1024 and a sink are required");
+  const hipError_t e = launch_empty(workgroups, threads, (uint32_t*)sink, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "empty launch");
+}
+
+int moe_w4a16_read_burst(const void* src, size_t bytes, int32_t loads_per_lane, void* sink,
+                         void* stream) {
+  if (!src || !sink) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  if (loads_per_lane != 1 && loads_per_lane != 2 && loads_per_lane != 4 && loads_per_lane != 8)
+    return fail(MOE_ERR_INVALID_ARG, "loads_per_lane must be 1, 2, 4 or 8");
+  if (bytes % 16 || !aligned(src, 16) || !aligned(sink, 4))
+    return fail(MOE_ERR_MISALIGNED, "src needs 16-byte alignment and a multiple of 16 bytes");
+  const hipError_t e = launch_read_burst(src, bytes, loads_per_lane, (uint32_t*)sink,
+                                         (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "read burst launch");
+}
+
 int moe_w4a16_dequant(const void* nibbles, const void* scales, int32_t rows, int32_t cols,
                       int32_t scale_fmt, void* out, void* stream) {
   if (!nibbles || !scales || !out) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
@@ -501,7 +563,7 @@ int run_route(const moe_w4a16_cfg* c, const void* x, const void* router_w, const
   const hipError_t e = launch_route(
       (const uint16_t*)x, (const uint16_t*)router_w, bias, T, c->hidden, c->num_experts, c->top_k,
       (c->flags & MOE_FLAG_PRENORM) != 0, c->prenorm_eps,
-      (double*)((uint8_t*)c->workspace + L.logits), (uint32_t*)((uint8_t*)c->workspace + L.rcount),
+      (double*)((uint8_t*)c->workspace + L.logits), (uint32_t*)((uint8_t*)c->workspace + kRouterCountOff),
       ids, (uint16_t*)rw, (hipStream_t)c->stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");
   return ok();

@@ -136,20 +136,6 @@ __global__ __launch_bounds__(256) void k_resolve(const int32_t* ids, const uint8
                         tsc ? tsc + (size_t)l * E * 2 : nullptr, i - l * per_layer, E, flags, err);
 }
 
-__device__ __forceinline__ SlotRef load_slot(const SlotRef* p) {
-  // one 32-byte vector load
-  SlotRef r;
-  const uint4* q = (const uint4*)p;
-  const uint4 a = q[0], b = q[1];
-  r.w = (const uint8_t*)(((uint64_t)a.y << 32) | a.x);
-  r.s = (const uint8_t*)(((uint64_t)a.w << 32) | a.z);
-  r.tg = __uint_as_float(b.x);
-  r.td = __uint_as_float(b.y);
-  r.ok = (int32_t)b.z;
-  r.pad = 0;
-  return r;
-}
-
 // Grouped gate/up GEMV + silu(g) * v.  A 256-thread workgroup is four
 // independent waves, each owning RW rows of gate and of up of one (token,
 // slot).  All loads of a wave are issued before any arithmetic; the

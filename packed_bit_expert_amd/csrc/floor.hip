@@ -1,0 +1,165 @@
+// Floor kernels for the decode path (measurement only).
+//
+// They answer how long the batch-1 decode kernels would take if they did no
+// arithmetic at all.  Each one reads exactly the bytes its decode kernel
+// reads, with the same grid, the same dependent load of the routing slot
+// before the weights, and the same order of loads per lane, then folds
+// everything it loaded into one word with XOR and writes nothing unless that
+// word equals an argument the host never passes (so the loads cannot be
+// dropped and no store traffic is added).  Next to them: an empty kernel of
+// a given grid (the launch alone), and a read of a byte range in which every
+// lane issues all of its 16-byte loads before it uses any (the cost of
+// moving the same bytes with no dependent load in front of them).
+//
+// The decode kernels they mirror are fixed to the LFM2.5-24B-A2B shape
+// (hidden 2048, expert intermediate 1536, top-4, E8M0 per 32): "LFM2.5-24B-A2B
+// -- Packed MXFP4 Inference", "Model and quantization".
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kH = 2048, kI = 1536, kK = 4;
+constexpr uint32_t kNever = 0x9E3779B9u;  // the word no fold is compared against in practice
+
+__device__ __forceinline__ uint32_t fold(const uint4& v) { return v.x ^ v.y ^ v.z ^ v.w; }
+
+// Gate/up: 4 waves per workgroup, wave gw owns rows 2 nb, 2 nb + 1 of gate and
+// of up of slot gw / 768; lane (li = lane % 16, q = lane / 16) loads one scale
+// byte and one 16-byte chunk of its row for chunks li, li + 16, li + 32,
+// li + 48; the workgroup loads the token's 4 KB of x (16 bytes per thread).
+__global__ __launch_bounds__(256) void k_floor_gateup(const SlotRef* pre, const uint16_t* x,
+                                                      uint32_t never, uint32_t* sink) {
+  asm volatile("" ::"s"(pre), "s"(x), "s"(never), "s"(sink));
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * 4 + wave;
+  const int per_slot = kI / 2;
+  const int nb = gw % per_slot, sj = gw / per_slot;
+  const SlotRef sr = load_slot(pre + sj);
+  __builtin_amdgcn_sched_barrier(0);
+  const uint4 xv = ldg16(x + 8 * threadIdx.x);
+  __builtin_amdgcn_sched_barrier(0);
+  const int li = lane & 15, q = lane >> 4;
+  const int n = nb * 2 + (q >> 1);
+  const uint8_t* srow = sr.s + (size_t)(q & 1) * kI * (kH / 32) + (size_t)n * (kH / 32);
+  const uint8_t* wrow = sr.w + (size_t)(q & 1) * kI * (kH / 2) + (size_t)n * (kH / 2);
+  uint32_t sv[4];
+  uint4 wv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sv[i] = ldg<uint8_t>(srow + li + 16 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wv[i] = ldg16(wrow + 16 * (li + 16 * i));
+  uint32_t acc = fold(xv);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc ^= sv[i] ^ fold(wv[i]);
+  if (acc == never) sink[gw & 4095] = acc;
+}
+
+// Down: 256 workgroups of 8 output rows, wave j = slot j; the workgroup loads
+// the token's h (k * I BF16, 16 bytes per thread three times), every thread
+// the 8 coefficients and one residual value; lane (li, q) loads the scale
+// byte and 16-byte chunk of rows m0 + q and m0 + 4 + q for chunks li,
+// li + 16, li + 32.
+__global__ __launch_bounds__(256) void k_floor_down(const SlotRef* pre, const uint16_t* hbuf,
+                                                    const uint16_t* rw, const uint16_t* residual,
+                                                    uint32_t never, uint32_t* sink) {
+  asm volatile("" ::"s"(pre), "s"(hbuf), "s"(rw), "s"(residual), "s"(never), "s"(sink));
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int m0 = blockIdx.x * 8;
+  const SlotRef sr = load_slot(pre + wave);
+  uint32_t acc = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc ^= rw[j < kK ? j : kK - 1];
+  acc ^= residual[m0 + tid % 8];
+  uint4 hv[3];
+#pragma unroll
+  for (int u = 0; u < 3; ++u) hv[u] = ldg16(hbuf + 8 * (tid + 256 * u));
+  const int li = lane & 15, q = lane >> 4;
+  const uint8_t* wd = sr.w + (size_t)kI * kH;
+  const uint8_t* sd = sr.s + 2 * (size_t)kI * (kH / 32);
+  uint32_t sv[2][3];
+  uint4 wv[2][3];
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      sv[st][i] = ldg<uint8_t>(sd + (size_t)(m0 + st * 4 + q) * (kI / 32) + li + 16 * i);
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      wv[st][i] = ldg16(wd + (size_t)(m0 + st * 4 + q) * (kI / 2) + 16 * (li + 16 * i));
+#pragma unroll
+  for (int u = 0; u < 3; ++u) acc ^= fold(hv[u]);
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int i = 0; i < 3; ++i) acc ^= sv[st][i] ^ fold(wv[st][i]);
+  if (acc == never) sink[(blockIdx.x * 4 + wave) & 4095] = acc;
+}
+
+__global__ void k_empty(uint32_t never, uint32_t* sink) {
+  if (blockIdx.x == never) sink[0] = 1u;
+}
+
+// Every lane issues its N loads (elements i, i + P, ..., i + (N - 1) P of the
+// n16 16-byte words, P the grid's thread count) before it uses any of them.
+template <int N>
+__global__ __launch_bounds__(256) void k_read_burst(const uint4* __restrict__ src, size_t n16,
+                                                    uint32_t never, uint32_t* sink) {
+  const size_t P = (size_t)gridDim.x * 256;
+  const size_t i0 = (size_t)blockIdx.x * 256 + threadIdx.x;
+  uint4 v[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const size_t i = i0 + (size_t)j * P;
+    v[j] = i < n16 ? ldg16(src + i) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  uint32_t acc = 0;
+#pragma unroll
+  for (int j = 0; j < N; ++j) acc ^= fold(v[j]);
+  if (acc == never) sink[i0 & 4095] = acc;
+}
+
+template <int N>
+hipError_t burst_n(const void* src, size_t n16, uint32_t* sink, hipStream_t s) {
+  const size_t grid = (n16 + (size_t)256 * N - 1) / ((size_t)256 * N);
+  return launch_kernel(MOE_KERNEL_READ_BURST, k_read_burst<N>, dim3((unsigned)grid), dim3(256), 0,
+                       s, (const uint4*)src, n16, kNever, sink);
+}
+
+}  // namespace
+
+bool decode_floor_supported(int H, int I, int K) { return H == kH && I == kI && K == kK; }
+
+hipError_t launch_decode_floor(const SlotRef* pre, const uint16_t* x, uint16_t* hbuf,
+                               const uint16_t* rw, const uint16_t* residual, uint32_t* sink,
+                               hipStream_t s) {
+  hipError_t e = launch_kernel(MOE_KERNEL_FLOOR_GATE_UP, k_floor_gateup, dim3(kK * kI / 2 / 4),
+                               dim3(256), 0, s, pre, x, kNever, sink);
+  if (e != hipSuccess) return e;
+  return launch_kernel(MOE_KERNEL_FLOOR_DOWN, k_floor_down, dim3(kH / 8), dim3(256), 0, s, pre,
+                       (const uint16_t*)hbuf, rw, residual, kNever, sink);
+}
+
+hipError_t launch_empty(int workgroups, int threads, uint32_t* sink, hipStream_t s) {
+  return launch_kernel(MOE_KERNEL_EMPTY, k_empty, dim3(workgroups), dim3(threads), 0, s, kNever,
+                       sink);
+}
+
+hipError_t launch_read_burst(const void* src, size_t bytes, int loads_per_lane, uint32_t* sink,
+                             hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  switch (loads_per_lane) {
+    case 1: return burst_n<1>(src, n16, sink, s);
+    case 2: return burst_n<2>(src, n16, sink, s);
+    case 4: return burst_n<4>(src, n16, sink, s);
+    case 8: return burst_n<8>(src, n16, sink, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace moe

@@ -168,6 +168,14 @@ int moe_w4a16_hybrid_forward(moe_w4a16_hybrid* h, const void* x, const int32_t* 
     return moe::report(MOE_ERR_INVALID_ARG, "scale_fmt unknown");
   if ((int64_t)cfg->inter * cfg->hidden * 3 / 2 != h->nib)
     return moe::report(MOE_ERR_INVALID_ARG, "nibble bytes do not match hidden / inter");
+  {
+    // the scales follow the nibbles in a triplet: one byte per 32 (E8M0) or
+    // 16 (E4M3) values of the three matrices
+    const int64_t grp = cfg->scale_fmt == MOE_SCALE_E4M3_G16 ? 16 : 32;
+    if (h->triplet < h->nib + (int64_t)3 * cfg->inter * cfg->hidden / grp)
+      return moe::report(MOE_ERR_INVALID_ARG,
+                         "triplet_bytes too small for the nibbles and scales of this scale_fmt");
+  }
   for (int e = 0; e < E; ++e)
     if (!resident_w[e] != !resident_s[e] || (!resident_w[e] && !host_src[e]))
       return moe::report(MOE_ERR_INVALID_ARG,

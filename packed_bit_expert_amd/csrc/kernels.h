@@ -18,6 +18,20 @@ struct SlotRef {
   int32_t ok, pad;
 };
 
+// A resolved slot with one 32-byte vector load (device code).
+__device__ __forceinline__ SlotRef load_slot(const SlotRef* p) {
+  SlotRef r;
+  const uint4* q = (const uint4*)p;
+  const uint4 a = q[0], b = q[1];
+  r.w = (const uint8_t*)(((uint64_t)a.y << 32) | a.x);
+  r.s = (const uint8_t*)(((uint64_t)a.w << 32) | a.z);
+  r.tg = __uint_as_float(b.x);
+  r.td = __uint_as_float(b.y);
+  r.ok = (int32_t)b.z;
+  r.pad = 0;
+  return r;
+}
+
 // Arguments of the per-token GEMV path (decode).  All pointers are device
 // pointers; the dump pointers may be null.
 struct DecodeArgs {
@@ -90,6 +104,16 @@ hipError_t launch_dequant(const uint8_t* nib, const uint8_t* sc, int rows, int c
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_delay(uint32_t microseconds, hipStream_t s);
+// Measurement kernels: the decode kernels' loads without their arithmetic
+// (hidden 2048, inter 1536, top-4, E8M0 only), an empty kernel, and a read in
+// which every lane issues all of its loads up front.
+bool decode_floor_supported(int H, int I, int K);
+hipError_t launch_decode_floor(const SlotRef* pre, const uint16_t* x, uint16_t* hbuf,
+                               const uint16_t* rw, const uint16_t* residual, uint32_t* sink,
+                               hipStream_t s);
+hipError_t launch_empty(int workgroups, int threads, uint32_t* sink, hipStream_t s);
+hipError_t launch_read_burst(const void* src, size_t bytes, int loads_per_lane, uint32_t* sink,
+                             hipStream_t s);
 bool router_supported(int H, int E, int K);
 // logits [T][E] FP64 and count [T] (zero, left zero) workspace; ids [T][K];
 // rw [T][K] BF16

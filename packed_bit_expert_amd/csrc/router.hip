@@ -98,10 +98,10 @@ __device__ void router_select(const double* logits, const float* bias, int E, in
 // wave holds the router-row pieces l, l + 64, ... (H a multiple of 512, at
 // most 2048: at most 4 pieces), loaded before x is waited for.  The
 // workgroup's logits leave together as device-coherent stores; once they
-// have completed, the workgroup counts itself in, and the token's last
-// workgroup to finish selects, reading the logits with device-coherent loads
-// -- an atomic count that nobody waits on, and no cache write-back or
-// invalidation.  count[T] starts at 0 and is left at 0.
+// have been stored, the workgroup counts itself in with a release atomic,
+// and the token's last workgroup to finish takes an acquire fence and
+// selects, reading the logits with device-coherent loads -- an atomic count
+// that nobody waits on.  count[T] starts at 0 and is left at 0.
 template <bool PRENORM>
 __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ x,
                                                 const uint16_t* __restrict__ wr,
@@ -173,13 +173,20 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ x,
       if ((int)blockIdx.y * 4 + w < E)
         __hip_atomic_store(logits + (size_t)t * E + blockIdx.y * 4 + w, lgs[w], __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-    // the logits are device-coherent stores: once they have completed, the
-    // count can be taken without writing back or invalidating any cache
-    __builtin_amdgcn_s_waitcnt(0);
-    const uint32_t prev = __hip_atomic_fetch_add(count + t, 1u, __ATOMIC_RELAXED,
+    // The count is a release operation at agent scope, so the logit stores
+    // above happen before it for every workgroup that reads the count; the
+    // workgroup that reads the final value takes an agent-scope acquire
+    // fence after it (fence synchronisation: its read of the count, part of
+    // every earlier workgroup's release sequence, is sequenced before the
+    // fence).  The workgroup barrier below then orders the selecting wave's
+    // logit loads after that acquire.
+    const uint32_t prev = __hip_atomic_fetch_add(count + t, 1u, __ATOMIC_RELEASE,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     last = prev == gridDim.y - 1;
-    if (last) __hip_atomic_store(count + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (last) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __hip_atomic_store(count + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   __syncthreads();
   if (!last || wave != 0) return;
@@ -196,12 +203,24 @@ bool router_supported(int H, int E, int K) {
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H,
                         int E, int K, bool prenorm, float eps, double* logits, uint32_t* count,
                         int32_t* ids, uint16_t* rw, hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  const dim3 grid(T, (E + 3) / 4);
-  return prenorm ? launch_kernel(MOE_KERNEL_ROUTER, k_router<true>, grid, dim3(256), 0, s, x, wr,
-                                 bias, H, E, K, eps, logits, count, ids, rw)
-                 : launch_kernel(MOE_KERNEL_ROUTER, k_router<false>, grid, dim3(256), 0, s, x, wr,
-                                 bias, H, E, K, eps, logits, count, ids, rw);
+  // at most kRouterCounters tokens per launch: their counters sit at a fixed
+  // place of the workspace, so a workspace reused with another cfg still
+  // finds them at zero; launches on one stream run one after the other
+  for (int t0 = 0; t0 < T; t0 += kRouterCounters) {
+    const int n = T - t0 < kRouterCounters ? T - t0 : kRouterCounters;
+    const dim3 grid(n, (E + 3) / 4);
+    const uint16_t* xc = x + (size_t)t0 * H;
+    double* lc = logits + (size_t)t0 * E;
+    int32_t* ic = ids + (size_t)t0 * K;
+    uint16_t* rc = rw + (size_t)t0 * K;
+    const hipError_t e =
+        prenorm ? launch_kernel(MOE_KERNEL_ROUTER, k_router<true>, grid, dim3(256), 0, s, xc, wr,
+                                bias, H, E, K, eps, lc, count, ic, rc)
+                : launch_kernel(MOE_KERNEL_ROUTER, k_router<false>, grid, dim3(256), 0, s, xc, wr,
+                                bias, H, E, K, eps, lc, count, ic, rc);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace moe

@@ -44,6 +44,7 @@ EXPORTS = [
     "moe_w4a16_timing_end", "moe_w4a16_route", "moe_w4a16_forward_routed",
     "moe_w4a16_stack_forward_routed", "moe_w4a16_hybrid_create", "moe_w4a16_hybrid_destroy",
     "moe_w4a16_hybrid_forward", "moe_w4a16_hybrid_stats", "moe_w4a16_hybrid_last_requests",
+    "moe_w4a16_decode_floor", "moe_w4a16_empty_launch", "moe_w4a16_read_burst",
 ]
 
 
@@ -67,7 +68,8 @@ KERNEL_KINDS = {1: "decode gate/up", 2: "decode down + combine", 3: "slot resolv
                 4: "batched gate/up GEMM", 5: "batched down GEMM", 6: "combine", 7: "sort",
                 8: "dequant", 9: "stream read", 10: "workspace fill", 11: "delay",
                 12: "router", 13: "pre-norm",
-                14: "x to MXFP4"}
+                14: "x to MXFP4", 15: "decode gate/up floor (loads only)",
+                16: "decode down floor (loads only)", 17: "empty kernel", 18: "burst read"}
 
 
 class Dump(C.Structure):
@@ -100,6 +102,9 @@ def lib():
             "moe_w4a16_device_status": (C.c_int, [P, C.POINTER(C.c_int32), P]),
             "moe_w4a16_stream_read": (C.c_int, [P, SZ, P, P]),
             "moe_w4a16_delay": (C.c_int, [C.c_uint32, P]),
+            "moe_w4a16_decode_floor": (C.c_int, [I32, P, P, P, P, P, P, C.POINTER(Cfg)]),
+            "moe_w4a16_empty_launch": (C.c_int, [I32, I32, P, P]),
+            "moe_w4a16_read_burst": (C.c_int, [P, SZ, I32, P, P]),
             "moe_w4a16_route": (C.c_int, [P, P, P, P, P, C.POINTER(Cfg)]),
             "moe_w4a16_forward_routed": (C.c_int, [P, P, P, P, P, P, P, P, C.POINTER(Cfg)]),
             "moe_w4a16_stack_forward_routed": (C.c_int, [I32, P, P, P, P, P, P, P, P, P,
@@ -243,6 +248,22 @@ def moe_w4a16_stream_read(src, nbytes, sink, stream=0):
 
 def moe_w4a16_delay(microseconds: int, stream=0):
     _check(lib().moe_w4a16_delay(microseconds, None if stream == 0 else _stream(stream)))
+
+
+def moe_w4a16_decode_floor(num_layers, x, expert_ids, route_w, packed_weights, scales, sink,
+                           cfg: Cfg):
+    _check(lib().moe_w4a16_decode_floor(num_layers, _p(x), _p(expert_ids), _p(route_w),
+                                        _p(packed_weights), _p(scales), _p(sink), C.byref(cfg)))
+
+
+def moe_w4a16_empty_launch(workgroups, threads, sink, stream=0):
+    _check(lib().moe_w4a16_empty_launch(workgroups, threads, _p(sink),
+                                        None if stream == 0 else _stream(stream)))
+
+
+def moe_w4a16_read_burst(src, nbytes, loads_per_lane, sink, stream=0):
+    _check(lib().moe_w4a16_read_burst(_p(src), nbytes, loads_per_lane, _p(sink),
+                                      None if stream == 0 else _stream(stream)))
 
 
 def moe_w4a16_timing_begin(capacity: int):

@@ -201,3 +201,33 @@ def test_hybrid_null_handle_errors():
     with pytest.raises(M.MoeError):
         M.moe_w4a16_hybrid_last_requests(None)
     M.moe_w4a16_hybrid_destroy(None)
+
+
+def test_floor_helpers_reject_bad_arguments():
+    """The decode floor mirrors only T = 1 at the 2048/1536/top-4 E8M0 shape;
+    the empty launch and the burst read check their own arguments."""
+    for over in ({"T": 2}, {"hidden": 1024, "inter": 768}, {"top_k": 2},
+                 {"scale_fmt": M.SCALE_E4M3_G16, "tensor_scales": FAKE}):
+        with pytest.raises(M.MoeError) as e:
+            M.moe_w4a16_decode_floor(38, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + (1 << 30), cfg(**over))
+        assert e.value.code in (M.ERR_UNSUPPORTED_SHAPE, M.ERR_INVALID_ARG), over
+    with pytest.raises(M.MoeError) as e:
+        M.moe_w4a16_decode_floor(0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + (1 << 30), cfg())
+    assert e.value.code == M.ERR_INVALID_ARG
+    with pytest.raises(M.MoeError) as e:
+        M.moe_w4a16_empty_launch(1, 2048, FAKE)
+    assert e.value.code == M.ERR_INVALID_ARG
+    with pytest.raises(M.MoeError) as e:
+        M.moe_w4a16_read_burst(FAKE, 4096, 3, FAKE)
+    assert e.value.code == M.ERR_INVALID_ARG
+    with pytest.raises(M.MoeError) as e:
+        M.moe_w4a16_read_burst(FAKE + 8, 4096, 4, FAKE)
+    assert e.value.code == M.ERR_MISALIGNED
+
+
+def test_workspace_control_words_do_not_move_with_cfg():
+    """The router's counters live in the control region at the start of every
+    workspace, so workspace sizes grow by the same fixed control region for
+    every cfg and a T = 1 workspace is never smaller than that region."""
+    b1 = M.moe_w4a16_workspace_bytes(cfg(T=1))
+    assert b1 >= 256 + 4 * 2048

@@ -146,3 +146,32 @@ def test_hybrid_errors(layer_mx):
         assert np.array_equal(out, res)
     finally:
         hy.close()
+
+
+def test_triplet_too_small_for_scale_format_rejected():
+    """A handle made for E8M0 triplets (4,718,592 + 294,912 bytes) called with
+    E4M3 scales (589,824 bytes per expert) is rejected before any copy or
+    launch: its staging slots could not hold the down scales."""
+    banner("hybrid: E8M0-sized triplets with an E4M3 cfg")
+    sh = LFM
+    nib = sh.nibble_bytes()
+    trip = nib + sh.scale_bytes(S.FMT_E8M0_G32)
+    staging = torch.empty((4, trip), dtype=torch.uint8, device=GH.dev())
+    h = M.moe_w4a16_hybrid_create(trip, nib, 8 * trip, 4, staging, sh.experts, 4)
+    try:
+        x = torch.zeros((1, sh.hidden), dtype=torch.bfloat16, device=GH.dev())
+        ids = GH.i32_dev(np.array([[0, 1, 2, 3]]))
+        rw = torch.zeros((1, 4), dtype=torch.bfloat16, device=GH.dev())
+        out = torch.empty_like(x)
+        ts = torch.ones((sh.experts, 2), dtype=torch.float32, device=GH.dev())
+        cfg = M.make_cfg(1, scale_fmt=S.FMT_E4M3_G16, tensor_scales=ts)
+        ws = torch.zeros(M.moe_w4a16_workspace_bytes(cfg), dtype=torch.uint8, device=GH.dev())
+        cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), ws.numel()
+        host = np.zeros(trip, np.uint8)
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_w4a16_hybrid_forward(h, x, ids, rw, [0] * sh.experts, [0] * sh.experts,
+                                       [host.ctypes.data] * sh.experts, out, cfg)
+        assert ei.value.code == M.ERR_INVALID_ARG
+        assert M.moe_w4a16_hybrid_stats(h)["h2d_bytes"] == 0
+    finally:
+        M.moe_w4a16_hybrid_destroy(h)

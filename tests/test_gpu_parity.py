@@ -40,14 +40,21 @@ def layer_nv():
 # -- bit-exact building blocks ------------------------------------------------------
 
 def test_dequant_e8m0_bitexact():
-    banner("dequant E8M0 codes 2..252, all nibbles")
-    codes = np.arange(2, 253, dtype=np.uint8)
+    """Every supported E8M0 code, 1..254, with every E2M1 code: code 1 with
+    the 0.5 nibble gives the BF16 subnormal 2^-127, and codes 253..254 with
+    large nibbles overflow to +-inf; both must come out exactly as the
+    oracle's correctly rounded values."""
+    banner("dequant E8M0 codes 1..254, all nibbles")
+    codes = np.arange(1, 255, dtype=np.uint8)
     rows, cols = codes.size, 256
     rng = np.random.default_rng(1)
     nib = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
-    nib[:, :8] = np.arange(256, dtype=np.uint8)[None, ::32].repeat(rows, 0)  # every code early
+    # every (low, high) nibble pair in the first block: all 16 codes at even
+    # and at odd positions under the row's own scale code
+    nib[:, :16] = (np.arange(16, dtype=np.uint8) | (np.arange(16, dtype=np.uint8)[::-1] << 4))[None, :]
     sc = np.repeat(codes[:, None], cols // 32, axis=1)
-    sc[:, 1:] = rng.integers(2, 253, size=(rows, cols // 32 - 1), dtype=np.uint8)
+    sc[:, 1:] = rng.integers(1, 255, size=(rows, cols // 32 - 1), dtype=np.uint8)
+    assert {int(c) for c in codes} <= set(np.unique(sc[:, 0]).tolist())
     out = torch.empty((rows, cols), dtype=torch.bfloat16, device=GH.dev())
     M.moe_w4a16_dequant(GH.u8_dev(nib), GH.u8_dev(sc), rows, cols, M.SCALE_E8M0_G32, out)
     torch.cuda.synchronize()

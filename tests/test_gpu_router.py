@@ -154,12 +154,62 @@ def _routed_stack(st, wrd, bd, x, L, T, flags=0):
     return GH.bits_host(out), ids.cpu().numpy()
 
 
+def _routed_layer_gpu(st, wrd, bd, h, l, T, flags=0):
+    """Layer l routed on the device from h (pre-norm + residual): out, ids, route_w."""
+    gl = torch.empty((T, LFM.hidden), dtype=torch.bfloat16, device=GH.dev())
+    gid = torch.empty((T, 4), dtype=torch.int32, device=GH.dev())
+    grw = torch.empty((T, 4), dtype=torch.bfloat16, device=GH.dev())
+    hd = GH.bf16_dev(h)
+    wt, stb, _ = st.layer_tables(l)
+    cfg = M.make_cfg(T, flags=M.FLAG_PRENORM | flags, residual=hd, prenorm_eps=GH.EPS)
+    ws = torch.zeros(M.moe_w4a16_workspace_bytes(cfg), dtype=torch.uint8, device=GH.dev())
+    cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), ws.numel()
+    M.moe_w4a16_forward_routed(hd, wrd[l], bd[l], wt, stb, gl, gid, grw, cfg)
+    torch.cuda.synchronize()
+    return GH.bits_host(gl), gid.cpu().numpy(), GH.bits_host(grw)
+
+
+def _teacher_forced(st, wr, b, wrd, bd, x, T, nlayers, flags=0):
+    """Layers 0..nlayers-1, each on the oracle chain's input h_l.  The GPU
+    routes and runs layer l on h_l.  Its ids must equal the oracle's, or tie
+    with them (check_ids); its coefficients must equal the oracle's where the
+    ids do, and follow the same rule on the oracle's logits where a tie gave
+    other ids.  The layer output is compared with the oracle's layer run on
+    the routing the GPU took (the oracle takes ids and coefficients as
+    inputs), so every layer is compared whatever the ties.  Returns the
+    number of layers and of tokens compared."""
+    w4a4 = bool(flags & M.FLAG_W4A4)
+    h = x
+    layers = tokens = 0
+    for l in range(nlayers):
+        lay = GH.Layer(LFM, S.FMT_E8M0_G32, l, store=st, l=l)
+        rids, rrw, lg = O.route(h, wr[l], b[l], top_k=4, prenorm=True, eps=GH.EPS, logits=True)
+        out, gids, grws = _routed_layer_gpu(st, wrd, bd, h, l, T, flags)
+        check_ids(gids, rids, lg, b[l], 4)
+        same = np.all(gids == rids, axis=1)
+        if same.any():
+            GH.compare(grws[same], rrw[same], f"layer {l} route_w")
+        if not same.all():
+            s = 1.0 / (1.0 + np.exp(-lg[~same]))
+            sel = np.take_along_axis(s, gids[~same].astype(np.int64), axis=1)
+            GH.compare(grws[~same], O.bf16_from_f64(sel / sel.sum(axis=1, keepdims=True)),
+                       f"layer {l} route_w at ties")
+        ids_ref = np.where(same[:, None], rids, gids).astype(np.int32)
+        rw_ref = np.where(same[:, None], rrw, grws).astype(np.uint16)
+        ref = lay.oracle(h, ids_ref, rw_ref, residual=h, prenorm=True, w4a4=w4a4)
+        GH.compare(out, ref, f"routed layer {l}" + (" w4a4" if w4a4 else ""))
+        layers += 1
+        tokens += T
+        h = ref if same.all() else lay.oracle(h, rids, rrw, residual=h, prenorm=True, w4a4=w4a4)
+    return layers, tokens
+
+
 @pytest.mark.parametrize("T", [1, 32])
 def test_routed_stack(routed_stack, T):
     """38 layers whose routing is computed on the device from each layer's
     input: the stack call equals 38 single-layer routed calls bit for bit,
-    and the first layers match the oracle (its own routing and layer) on the
-    oracle chain's input."""
+    and the first layers, teacher-forced on the oracle chain, match the
+    oracle's routing and layer."""
     st, wr, b, wrd, bd = routed_stack
     L = LFM.layers
     banner(f"routed 38-layer stack T={T}")
@@ -167,26 +217,9 @@ def test_routed_stack(routed_stack, T):
     got, ids = _routed_stack(st, wrd, bd, x, L, T)
     chain, ids_c = _routed_single(st, wrd, bd, x, L, T)
     assert np.array_equal(got, chain) and np.array_equal(ids, ids_c)
-    h = x
-    for l in range(4 if T == 32 else 8):
-        lay = GH.Layer(LFM, S.FMT_E8M0_G32, l, store=st, l=l)
-        rids, rrw, lg = O.route(h, wr[l], b[l], top_k=4, prenorm=True, eps=GH.EPS, logits=True)
-        nxt = lay.oracle(h, rids, rrw, residual=h, prenorm=True)
-        # the GPU routes and runs layer l on the oracle chain's h_l
-        gl = torch.empty((T, LFM.hidden), dtype=torch.bfloat16, device=GH.dev())
-        gid = torch.empty((T, 4), dtype=torch.int32, device=GH.dev())
-        grw = torch.empty((T, 4), dtype=torch.bfloat16, device=GH.dev())
-        hd = GH.bf16_dev(h)
-        wt, stb, _ = st.layer_tables(l)
-        cfg = M.make_cfg(T, flags=M.FLAG_PRENORM, residual=hd, prenorm_eps=GH.EPS)
-        ws = torch.zeros(M.moe_w4a16_workspace_bytes(cfg), dtype=torch.uint8, device=GH.dev())
-        cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), ws.numel()
-        M.moe_w4a16_forward_routed(hd, wrd[l], bd[l], wt, stb, gl, gid, grw, cfg)
-        torch.cuda.synchronize()
-        check_ids(gid.cpu().numpy(), rids, lg, b[l], 4)
-        if np.array_equal(gid.cpu().numpy(), rids):
-            GH.compare(GH.bits_host(gl), nxt, f"routed layer {l}")
-        h = nxt
+    n = 4 if T == 32 else 8
+    layers, tokens = _teacher_forced(st, wr, b, wrd, bd, x, T, n)
+    assert (layers, tokens) == (n, n * T)
 
 
 def test_routed_stack_w4a4(routed_stack):
@@ -194,7 +227,8 @@ def test_routed_stack_w4a4(routed_stack):
     writes the next layer's pre-normed input as MXFP4 rows, which the next
     layer's gate/up stages as they are (its router reads the layer input).
     The stack equals 8 single-layer routed W4A4 calls bit for bit, and the
-    first layer matches the oracle's routing and W4A4 layer."""
+    first 4 layers, teacher-forced on the oracle's W4A4 chain, match the
+    oracle's routing and W4A4 layer."""
     st, wr, b, wrd, bd = routed_stack
     L, T = 8, 32
     banner(f"routed W4A4 stack L={L} T={T}")
@@ -202,13 +236,56 @@ def test_routed_stack_w4a4(routed_stack):
     got, ids = _routed_stack(st, wrd, bd, x, L, T, flags=M.FLAG_W4A4)
     chain, ids_c = _routed_single(st, wrd, bd, x, L, T, flags=M.FLAG_W4A4)
     assert np.array_equal(got, chain) and np.array_equal(ids, ids_c)
-    rids, rrw, lg = O.route(x, wr[0], b[0], top_k=4, prenorm=True, eps=GH.EPS, logits=True)
-    check_ids(ids[0], rids, lg, b[0], 4)
-    if np.array_equal(ids[0], rids):
-        lay = GH.Layer(LFM, S.FMT_E8M0_G32, 0, store=st, l=0)
-        ref = lay.oracle(x, rids, rrw, residual=x, prenorm=True, w4a4=True)
-        g1, _ = _routed_single(st, wrd, bd, x, 1, T, flags=M.FLAG_W4A4)
-        GH.compare(g1, ref, "routed w4a4 layer 0")
+    layers, tokens = _teacher_forced(st, wr, b, wrd, bd, x, T, 4, flags=M.FLAG_W4A4)
+    assert (layers, tokens) == (4, 4 * T)
+
+
+def test_router_coefficients_hand_worked():
+    """The hand-worked coefficient case of the oracle's pins on the device:
+    logits (0, bf16(ln 3), -2) select experts (1, 0) with coefficients
+    0x3F1A (0.6015625) and 0x3ECD (0.400390625)."""
+    banner("router hand-worked coefficients")
+    H, E = 512, 3
+    x = np.zeros((1, H), np.uint16)
+    x[0, 0] = 0x3F80
+    w = np.zeros((E, H), np.uint16)
+    w[1, 0] = 0x3F8D
+    w[2, 0] = 0xC000
+    ids, rw = route_gpu(x, w, None, 2, E=E)
+    assert ids[0].tolist() == [1, 0]
+    assert rw[0].tolist() == [0x3F1A, 0x3ECD]
+
+
+def test_workspace_reused_across_cfgs(routed_stack):
+    """One workspace, zeroed once and sized for the largest call, serves a
+    routed T = 32 call and then a routed T = 1 call (with MOE_FLAG_CHECK_IDS):
+    the router's counters sit at a fixed place, so the second call still
+    routes, and both match the oracle."""
+    st, wr, b, wrd, bd = routed_stack
+    banner("one workspace for routed T=32 then T=1 calls")
+    c32 = M.make_cfg(32, flags=M.FLAG_PRENORM | M.FLAG_CHECK_IDS, prenorm_eps=GH.EPS)
+    nbytes = M.moe_w4a16_workspace_bytes(c32)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=GH.dev())
+    for T, l, seed in ((32, 2, 31), (1, 3, 32), (32, 4, 33), (1, 5, 34)):
+        x = S.activations(FAMILY, 0, seed, T, LFM.hidden)
+        hd = GH.bf16_dev(x)
+        cfg = M.make_cfg(T, flags=M.FLAG_PRENORM | M.FLAG_CHECK_IDS, residual=hd,
+                         prenorm_eps=GH.EPS)
+        assert M.moe_w4a16_workspace_bytes(cfg) <= nbytes
+        cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), nbytes
+        out = torch.empty((T, LFM.hidden), dtype=torch.bfloat16, device=GH.dev())
+        gid = torch.full((T, 4), -1, dtype=torch.int32, device=GH.dev())
+        grw = torch.zeros((T, 4), dtype=torch.bfloat16, device=GH.dev())
+        wt, stb, _ = st.layer_tables(l)
+        M.moe_w4a16_forward_routed(hd, wrd[l], bd[l], wt, stb, out, gid, grw, cfg)
+        torch.cuda.synchronize()
+        assert M.moe_w4a16_device_status(ws) == 0
+        gids, grws = gid.cpu().numpy(), GH.bits_host(grw)
+        rids, rrw, lg = O.route(x, wr[l], b[l], top_k=4, prenorm=True, eps=GH.EPS, logits=True)
+        check_ids(gids, rids, lg, b[l], 4)
+        lay = GH.Layer(LFM, S.FMT_E8M0_G32, l, store=st, l=l)
+        GH.compare(GH.bits_host(out), lay.oracle(x, gids, grws, residual=x, prenorm=True),
+                   f"reused workspace T={T}")
 
 
 def test_routed_stack_graph_replay(routed_stack):

@@ -137,3 +137,28 @@ def test_router_rejects_bad_k():
     w = np.zeros((4, 32), np.uint16)
     with pytest.raises(ValueError):
         O.route(x, w, top_k=5)
+
+
+def test_coefficients_hand_worked_normalised_scores():
+    """A hand-worked value that separates the coefficient rule (selected
+    sigmoid scores normalised to sum 1) from a softmax over the selected
+    logits.  x = e_0 and router rows whose first entries are 0, bf16(ln 3) =
+    1.1015625 and -2 give logits (0, 1.1015625, -2).  Scores: sigmoid(0) =
+    1/2 and sigmoid(1.1015625) = 1 / (1 + e^-1.1015625) = 0.750553 (ln 3
+    would give exactly 3/4), so the top-2 slots are experts (1, 0) with
+    coefficients 0.750553 / 1.250553 = 0.600177 and 0.399823 (exactly 0.6 and
+    0.4 at ln 3).  Rounded to BF16 (spacing 2^-8 on [1/2, 1), 2^-9 on
+    [1/4, 1/2)): 154 * 2^-8 = 0.6015625 (0x3F1A) and 205 * 2^-9 =
+    0.400390625 (0x3ECD).  A softmax of the two logits would give 0.7505 and
+    0.2495 instead."""
+    H, E = 512, 3
+    x = np.zeros((1, H), np.uint16)
+    x[0, 0] = 0x3F80  # 1.0
+    w = np.zeros((E, H), np.uint16)
+    w[1, 0] = 0x3F8D  # 1.1015625, the BF16 nearest to ln 3
+    w[2, 0] = 0xC000  # -2.0
+    assert O.f64_from_bf16(np.array([0x3F8D], np.uint16))[0] == 1.1015625
+    ids, rw, lg = O.route(x, w, top_k=2, logits=True)
+    assert lg[0].tolist() == [0.0, 1.1015625, -2.0]
+    assert ids[0].tolist() == [1, 0]
+    assert rw[0].tolist() == [0x3F1A, 0x3ECD]
