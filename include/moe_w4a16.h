@@ -190,6 +190,26 @@ int moe_w4a16_forward_debug(const void* x, const int32_t* expert_ids, const void
                             void* out, const moe_w4a16_cfg* cfg, const moe_w4a16_dump* dump);
 
 /*
+ * moe_w4a16_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same layer, the same kernels and the same results, with
+ * cfg->workspace and cfg->workspace_bytes ignored.  The workspace is a
+ * file-scope device array of the library, 4 MiB (4,194,304 bytes) on each
+ * GPU it runs on, held until the process ends; the call allocates and frees
+ * nothing.  A call whose moe_w4a16_workspace_bytes(cfg) exceeds 4 MiB (at
+ * hidden 2048 / inter 1536 / 64 experts / top-4: more than 77 tokens) fails
+ * with MOE_ERR_WORKSPACE_TOO_SMALL before anything is enqueued;
+ * MOE_FLAG_CHECK_IDS is rejected (MOE_ERR_INVALID_ARG: its error word would
+ * have no reader).  Every call on one GPU shares that GPU's array, and no
+ * part of it needs to start at zero (each call writes every region before it
+ * reads it), but calls that overlap in time on one GPU -- on different
+ * streams, or from different threads without ordering -- race on it.
+ */
+int moe_w4a16_forward_noalloc(const void* x, const int32_t* expert_ids, const void* route_w,
+                              const void* const* packed_weights, const void* const* scales,
+                              void* out, const moe_w4a16_cfg* cfg);
+
+/*
  * L chained MoE layers (the 38-layer MoE stack of LFM2.5-24B-A2B, "Model and
  * quantization": 40 layers of which 38 are MoE), batch T:
  *     h_0 = x;  h_{l+1} = bf16(h_l + MoE_l(prenorm(h_l)));  out = h_L

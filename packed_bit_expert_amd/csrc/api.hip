@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "common.h"
@@ -721,4 +722,73 @@ extern "C" int moe_w4a16_delay(uint32_t microseconds, void* stream) {
   const hipError_t e = launch_delay(microseconds, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "delay launch");
   return ok();
+}
+
+// ---------------------------------------------------------------------------
+// moe_w4a16_forward_noalloc: moe_w4a16_forward without a caller workspace,
+// for callers that cannot allocate device memory.  The workspace regions
+// (h, y, the pre-normed input, the routing slots, ...) live in one
+// file-scope device array per GPU; nothing is allocated or freed.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+// The array's device address on each GPU (the name is only a host-side
+// stand-in), looked up once per device with that device current.
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_INVALID_ARG, "device %d beyond the %d the no-alloc entry point serves", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || !aligned(p, 256)) return fail(MOE_ERR_HIP, "scratch array address unusable");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int moe_w4a16_forward_noalloc(const void* x, const int32_t* expert_ids,
+                                         const void* route_w, const void* const* packed_weights,
+                                         const void* const* scales, void* out,
+                                         const moe_w4a16_cfg* cfg) {
+  int rc = check_shape(cfg);
+  if (rc) return rc;
+  if (cfg->flags & MOE_FLAG_CHECK_IDS)
+    return fail(MOE_ERR_INVALID_ARG,
+                "MOE_FLAG_CHECK_IDS is not available without a caller workspace (the error word "
+                "would have no reader)");
+  const size_t need = moe_w4a16_workspace_bytes(cfg);
+  if (need > kNoAllocScratchBytes)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL,
+                "this call needs %zu bytes of workspace; the no-alloc entry point has %zu "
+                "(fewer tokens per call, or moe_w4a16_forward with a workspace)",
+                need, kNoAllocScratchBytes);
+  if (cfg->num_tokens == 0) return ok();
+  void* ws = nullptr;
+  rc = scratch_of_current_device(&ws);
+  if (rc) return rc;
+  moe_w4a16_cfg lc = *cfg;
+  lc.workspace = ws;
+  lc.workspace_bytes = kNoAllocScratchBytes;
+  Call k{x, expert_ids, route_w, packed_weights, scales, lc.tensor_scales, lc.residual, out,
+         nullptr};
+  rc = check_call(&lc, k);
+  if (rc) return rc;
+  return run_layer(&lc, k);
 }

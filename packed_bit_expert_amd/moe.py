@@ -45,6 +45,7 @@ EXPORTS = [
     "moe_w4a16_stack_forward_routed", "moe_w4a16_hybrid_create", "moe_w4a16_hybrid_destroy",
     "moe_w4a16_hybrid_forward", "moe_w4a16_hybrid_stats", "moe_w4a16_hybrid_last_requests",
     "moe_w4a16_decode_floor", "moe_w4a16_empty_launch", "moe_w4a16_read_burst",
+    "moe_w4a16_forward_noalloc",
 ]
 
 
@@ -95,6 +96,7 @@ def lib():
             "moe_w4a16_workspace_init": (C.c_int, [P, SZ, P]),
             "moe_w4a16_forward": (C.c_int, [P, P, P, P, P, P, C.POINTER(Cfg)]),
             "moe_w4a16_forward_debug": (C.c_int, [P, P, P, P, P, P, C.POINTER(Cfg), C.POINTER(Dump)]),
+            "moe_w4a16_forward_noalloc": (C.c_int, [P, P, P, P, P, P, C.POINTER(Cfg)]),
             "moe_w4a16_stack_forward": (C.c_int, [I32, P, P, P, P, P, P, P, C.POINTER(Cfg)]),
             "moe_w4a16_dequant": (C.c_int, [P, P, I32, I32, I32, P, P]),
             "moe_w4a16_combine": (C.c_int, [P, P, P, P, I32, I32, I32, P]),
@@ -200,6 +202,11 @@ def moe_w4a16_workspace_init(workspace, nbytes: int, stream=0):
 def moe_w4a16_forward(x, expert_ids, route_w, packed_weights, scales, out, cfg: Cfg):
     _check(lib().moe_w4a16_forward(_p(x), _p(expert_ids), _p(route_w), _p(packed_weights),
                                    _p(scales), _p(out), C.byref(cfg)))
+
+
+def moe_w4a16_forward_noalloc(x, expert_ids, route_w, packed_weights, scales, out, cfg: Cfg):
+    _check(lib().moe_w4a16_forward_noalloc(_p(x), _p(expert_ids), _p(route_w),
+                                           _p(packed_weights), _p(scales), _p(out), C.byref(cfg)))
 
 
 def moe_w4a16_forward_debug(x, expert_ids, route_w, packed_weights, scales, out, cfg: Cfg,
