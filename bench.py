@@ -145,12 +145,46 @@ def decode_floor(args, store, stream, dev, xs, ids, rws, cfg, warmup, steps, buf
 
     empty = {"1": timed(lambda i: M.moe_w4a16_empty_launch(768, 256, sink, stream)),
              "2": timed(lambda i: M.moe_w4a16_empty_launch(256, 256, sink, stream))}
+
+    # the same two floors inside a captured graph, as the step itself runs:
+    # the decode launches of a step with no arithmetic, and as many empty
+    # kernels of the same grids as a step launches
+    import torch
+
+    def graph_ms(fn, nrep):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for r in range(nrep):
+                fn(r)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / nrep
+
+    floor_step_ms = graph_ms(lambda r: M.moe_w4a16_decode_floor(
+        L, xs[warmup + r], ids[warmup + r], rws[warmup + r], store.wtab, store.stab, sink, cfg),
+        steps)
+
+    def empty_step(r):
+        M.moe_w4a16_empty_launch(256, 64, sink, stream)  # the slot resolve's place
+        for _ in range(L):
+            M.moe_w4a16_empty_launch(768, 256, sink, stream)
+            M.moe_w4a16_empty_launch(256, 256, sink, stream)
+
+    empty_step_ms = graph_ms(empty_step, steps)
     burst = {}
     for kind, nb in (("1", 13373440), ("2", 6692864)):
         nreg = buf.numel() // nb
         burst[kind] = {str(lpl): timed(lambda i, lpl=lpl: M.moe_w4a16_read_burst(
             buf.data_ptr() + (i % nreg) * nb, nb, lpl, sink, stream)) for lpl in (1, 2, 4, 8)}
     return {"loads_only_us": loads_only, "empty_us": empty, "burst_read_us": burst,
+            "graph_loads_only_step_ms": floor_step_ms, "graph_empty_step_ms": empty_step_ms,
+            "launches_per_step": 2 * L + 1,
             "burst_read_best_us": {k: min(v.values()) for k, v in burst.items()},
             "note": "kinds: 1 = decode gate/up (13,373,440 B per launch), 2 = decode down + "
                     "combine (6,692,864 B per launch)"}

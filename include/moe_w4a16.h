@@ -330,8 +330,10 @@ int moe_w4a16_stream_read(const void* src, size_t bytes, void* sink, void* strea
  *   16-byte aligned) in which each layer's two decode kernels are replaced
  *   by kernels with the same grid that resolve the same routing slots and
  *   issue the same loads in the same order -- the selected experts' nibbles
- *   and scales, x, h, the coefficients and the residual -- and only fold
- *   them with XOR (no dequantisation, no products, no stores).  Only the
+ *   and scales, x, h, the coefficients and the residual -- fold them with
+ *   XOR (no dequantisation, no products, no reductions) and store the fold
+ *   where the decode kernels store h (in the workspace) and out (here in
+ *   `sink`).  Only the
  *   LFM2.5-24B-A2B shape (hidden 2048, inter 1536, top-4) with E8M0 scales;
  *   otherwise MOE_ERR_UNSUPPORTED_SHAPE.
  * moe_w4a16_empty_launch: one kernel of `workgroups` x `threads` (1..1024)

@@ -432,7 +432,7 @@ int moe_w4a16_decode_floor(int32_t num_layers, const void* x, const int32_t* exp
     hipError_t e = launch_decode_floor(slots + (size_t)g * T * K, (const uint16_t*)src,
                                        (uint16_t*)(ws + L.hbuf),
                                        (const uint16_t*)route_w + (size_t)l * T * K,
-                                       (const uint16_t*)src, (uint32_t*)sink, s);
+                                       (const uint16_t*)src, (uint16_t*)sink, s);
     if (e != hipSuccess) return hip_fail(e, "decode floor launch");
     src = (l % 2 == 0) ? (const void*)(ws + L.ping) : x;
   }

@@ -4,12 +4,13 @@
 // arithmetic at all.  Each one reads exactly the bytes its decode kernel
 // reads, with the same grid, the same dependent load of the routing slot
 // before the weights, and the same order of loads per lane, then folds
-// everything it loaded into one word with XOR and writes nothing unless that
-// word equals an argument the host never passes (so the loads cannot be
-// dropped and no store traffic is added).  Next to them: an empty kernel of
-// a given grid (the launch alone), and a read of a byte range in which every
-// lane issues all of its 16-byte loads before it uses any (the cost of
-// moving the same bytes with no dependent load in front of them).
+// everything it loaded into one word with XOR, which it stores where its
+// decode kernel stores its results (h, out), so that the loads cannot be
+// dropped and the same stores complete before the kernel ends.  Next to
+// them: an empty kernel of a given grid (the launch alone), and a read of a
+// byte range in which every lane issues all of its 16-byte loads before it
+// uses any (the cost of moving the same bytes with no dependent load in
+// front of them).
 //
 // The decode kernels they mirror are fixed to the LFM2.5-24B-A2B shape
 // (hidden 2048, expert intermediate 1536, top-4, E8M0 per 32): "LFM2.5-24B-A2B
@@ -31,8 +32,8 @@ __device__ __forceinline__ uint32_t fold(const uint4& v) { return v.x ^ v.y ^ v.
 // byte and one 16-byte chunk of its row for chunks li, li + 16, li + 32,
 // li + 48; the workgroup loads the token's 4 KB of x (16 bytes per thread).
 __global__ __launch_bounds__(256) void k_floor_gateup(const SlotRef* pre, const uint16_t* x,
-                                                      uint32_t never, uint32_t* sink) {
-  asm volatile("" ::"s"(pre), "s"(x), "s"(never), "s"(sink));
+                                                      uint16_t* hbuf) {
+  asm volatile("" ::"s"(pre), "s"(x), "s"(hbuf));
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int gw = blockIdx.x * 4 + wave;
   const int per_slot = kI / 2;
@@ -54,7 +55,8 @@ __global__ __launch_bounds__(256) void k_floor_gateup(const SlotRef* pre, const 
   uint32_t acc = fold(xv);
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc ^= sv[i] ^ fold(wv[i]);
-  if (acc == never) sink[gw & 4095] = acc;
+  // the decode kernel's stores: h of rows n (lane 0) and n + 1 (lane 32)
+  if (li == 0 && (q & 1) == 0) hbuf[(size_t)sj * kI + n] = (uint16_t)acc;
 }
 
 // Down: 256 workgroups of 8 output rows, wave j = slot j; the workgroup loads
@@ -64,8 +66,8 @@ __global__ __launch_bounds__(256) void k_floor_gateup(const SlotRef* pre, const 
 // li + 16, li + 32.
 __global__ __launch_bounds__(256) void k_floor_down(const SlotRef* pre, const uint16_t* hbuf,
                                                     const uint16_t* rw, const uint16_t* residual,
-                                                    uint32_t never, uint32_t* sink) {
-  asm volatile("" ::"s"(pre), "s"(hbuf), "s"(rw), "s"(residual), "s"(never), "s"(sink));
+                                                    uint16_t* out) {
+  asm volatile("" ::"s"(pre), "s"(hbuf), "s"(rw), "s"(residual), "s"(out));
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m0 = blockIdx.x * 8;
   const SlotRef sr = load_slot(pre + wave);
@@ -97,7 +99,8 @@ __global__ __launch_bounds__(256) void k_floor_down(const SlotRef* pre, const ui
   for (int st = 0; st < 2; ++st)
 #pragma unroll
     for (int i = 0; i < 3; ++i) acc ^= sv[st][i] ^ fold(wv[st][i]);
-  if (acc == never) sink[(blockIdx.x * 4 + wave) & 4095] = acc;
+  // the decode kernel's stores: one output value per row of the workgroup
+  if (tid < 8) out[m0 + tid] = (uint16_t)acc;
 }
 
 __global__ void k_empty(uint32_t never, uint32_t* sink) {
@@ -135,13 +138,13 @@ hipError_t burst_n(const void* src, size_t n16, uint32_t* sink, hipStream_t s) {
 bool decode_floor_supported(int H, int I, int K) { return H == kH && I == kI && K == kK; }
 
 hipError_t launch_decode_floor(const SlotRef* pre, const uint16_t* x, uint16_t* hbuf,
-                               const uint16_t* rw, const uint16_t* residual, uint32_t* sink,
+                               const uint16_t* rw, const uint16_t* residual, uint16_t* out,
                                hipStream_t s) {
   hipError_t e = launch_kernel(MOE_KERNEL_FLOOR_GATE_UP, k_floor_gateup, dim3(kK * kI / 2 / 4),
-                               dim3(256), 0, s, pre, x, kNever, sink);
+                               dim3(256), 0, s, pre, x, hbuf);
   if (e != hipSuccess) return e;
   return launch_kernel(MOE_KERNEL_FLOOR_DOWN, k_floor_down, dim3(kH / 8), dim3(256), 0, s, pre,
-                       (const uint16_t*)hbuf, rw, residual, kNever, sink);
+                       (const uint16_t*)hbuf, rw, residual, out);
 }
 
 hipError_t launch_empty(int workgroups, int threads, uint32_t* sink, hipStream_t s) {

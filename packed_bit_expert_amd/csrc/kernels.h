@@ -109,7 +109,7 @@ hipError_t launch_delay(uint32_t microseconds, hipStream_t s);
 // which every lane issues all of its loads up front.
 bool decode_floor_supported(int H, int I, int K);
 hipError_t launch_decode_floor(const SlotRef* pre, const uint16_t* x, uint16_t* hbuf,
-                               const uint16_t* rw, const uint16_t* residual, uint32_t* sink,
+                               const uint16_t* rw, const uint16_t* residual, uint16_t* out,
                                hipStream_t s);
 hipError_t launch_empty(int workgroups, int threads, uint32_t* sink, hipStream_t s);
 hipError_t launch_read_burst(const void* src, size_t bytes, int loads_per_lane, uint32_t* sink,
