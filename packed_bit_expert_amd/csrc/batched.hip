@@ -118,7 +118,8 @@ constexpr int kWgPerCu[2] = {2, 3};
 template <int FMT, int NMAT>
 struct WStep {
   uint4 w[NMAT][2];
-  uint32_t s[NMAT];  // this lane's scales of the step (E8M0: filled from StageScales)
+  uint32_t s[NMAT];  // E8M0: this lane's two scale bytes of the step (filled from StageScales)
+  uint4 s16[FMT == MOE_SCALE_E4M3_G16 ? NMAT : 1];  // E4M3: the row's 16 scale bytes of the step
 };
 
 // E8M0 scales of one stage, 8 bytes (one K step of a row) per step, loaded 16
@@ -160,9 +161,10 @@ __device__ __forceinline__ void load_wstep(WStep<FMT, NMAT>& st, const uint8_t* 
                                            bool ok) {
   const int wo = ok ? ks * (kKS / 2) + 32 * g : 0;
   if constexpr (FMT == MOE_SCALE_E4M3_G16) {
+    // all 16 scale groups of the row's step: after the pair swap below a
+    // lane accumulates MFMA results of every group of its row
 #pragma unroll
-    for (int mt = 0; mt < NMAT; ++mt)
-      st.s[mt] = ldg<uint32_t>(srow[mt] + (ok ? ks * (kKS / 16) + 4 * g : 0));
+    for (int mt = 0; mt < NMAT; ++mt) st.s16[mt] = ldg16(srow[mt] + (ok ? ks * (kKS / 16) : 0));
   }
 #pragma unroll
   for (int mt = 0; mt < NMAT; ++mt) {
@@ -173,13 +175,19 @@ __device__ __forceinline__ void load_wstep(WStep<FMT, NMAT>& st, const uint8_t* 
 }
 
 template <int FMT, int NMAT>
-__device__ __forceinline__ bf16x8 wstep_operand(const WStep<FMT, NMAT>& st, int mt, int d) {
+__device__ __forceinline__ uint32_t wstep_dword(const WStep<FMT, NMAT>& st, int mt, int d) {
   const uint4& h = st.w[mt][d >> 2];
-  const uint32_t w = (d & 3) == 0 ? h.x : (d & 3) == 1 ? h.y : (d & 3) == 2 ? h.z : h.w;
-  if constexpr (FMT == MOE_SCALE_E8M0_G32)
-    return fp4x8_to_bf16x8(w, e8m0_f32((st.s[mt] >> (8 * (d >> 2))) & 255u));
-  else
-    return fp4x8_scaled_to_bf16x8(w, e4m3_f32((st.s[mt] >> (8 * (d >> 1))) & 255u));
+  return (d & 3) == 0 ? h.x : (d & 3) == 1 ? h.y : (d & 3) == 2 ? h.z : h.w;
+}
+
+template <int FMT, int NMAT>
+__device__ __forceinline__ bf16x8 wstep_operand(const WStep<FMT, NMAT>& st, int mt, int d) {
+  return fp4x8_to_bf16x8(wstep_dword(st, mt, d), e8m0_f32((st.s[mt] >> (8 * (d >> 2))) & 255u));
+}
+
+__device__ __forceinline__ uint32_t byte_of(const uint4& v, int b) {
+  const uint32_t w = (b >> 2) == 0 ? v.x : (b >> 2) == 1 ? v.y : (b >> 2) == 2 ? v.z : v.w;
+  return (w >> (8 * (b & 3))) & 255u;
 }
 
 // One K step: 8 MFMAs per matrix on one 16-token tile (E8M0; E4M3 below).  Each MFMA's FP32
@@ -188,9 +196,12 @@ __device__ __forceinline__ bf16x8 wstep_operand(const WStep<FMT, NMAT>& st, int 
 // Chaining MFMAs in FP32 instead is cheaper but flips output roundings often
 // enough that the slot-order BF16 combine, where slots cancel, turns a flip
 // into an error above the 1% parity bound.
+// E8M0: arow = the lane's token row at its lane group's K slice of the step.
+// E4M3: arow = the lane's token row at the start of the step, and zrow a
+// 16-byte zero block in LDS.
 template <int FMT, int NMAT>
 __device__ __forceinline__ void wstep_mfma(const WStep<FMT, NMAT>& st, const uint16_t* arow,
-                                           double (&acc)[2][4]) {
+                                           const uint16_t* zrow, double (&acc)[2][4]) {
   if constexpr (FMT == MOE_SCALE_E8M0_G32) {
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
@@ -204,33 +215,49 @@ __device__ __forceinline__ void wstep_mfma(const WStep<FMT, NMAT>& st, const uin
       }
     }
   } else {
-    // E4M3: the four lane groups' slices of one MFMA carry four different
-    // scales, whose ratios reach 2^14, and an FP32 sum across them rounds
-    // often enough to break the parity bound where the slots cancel.  Each
-    // lane group's slices get MFMAs of their own (the other lanes give
-    // zeros); MFMAs d = 2j and 2j + 1 of a lane group read one 16-value scale
-    // group, so they are chained in FP32 and added to FP64 once: every FP32
-    // sum stays inside one scale group, as with E8M0.
-    const bf16x8 Z = {};
-    const int q0 = (int)(threadIdx.x & 63) >> 4;  // this lane's group
+    // E4M3: the scale groups are 16 values and their scales differ by up to
+    // 2^14 within a row, so an FP32 sum across groups rounds often enough to
+    // break the parity bound where the slots cancel: every MFMA must sum one
+    // group only.  Lane group g loaded the step's groups 4g .. 4g + 3, group
+    // 4g + j in dwords 2j (its first 8 values) and 2j + 1 (its last 8).  One
+    // gfx950 permlane16 swap per pair of dwords exchanges the second dword of
+    // lane groups 0 and 2 with the first dword of lane groups 1 and 3, after
+    // which dword 2j holds group j in lane groups 0 | 1 (first | last 8
+    // values) and group 8 + j in lane groups 2 | 3, and dword 2j + 1 holds
+    // groups 4 + j and 12 + j the same way.  Each dword then feeds two
+    // MFMAs, one per group: the lane groups of the other group read a zero
+    // block as their A operand.  The codes go in unscaled (exact in BF16),
+    // each MFMA sums 16 products of one group in FP32, and its result is
+    // scaled by the group's E4M3 value in FP64 (exact product, one rounding
+    // in the add).
+    const int gl = (int)(threadIdx.x & 63) >> 4;  // this lane's group
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16x8 A0 = *(const bf16x8*)(arow + 16 * j);
-      const bf16x8 A1 = *(const bf16x8*)(arow + 16 * j + 8);
+    for (int mt = 0; mt < NMAT; ++mt) {
+      uint32_t dw[8];
 #pragma unroll
-      for (int mt = 0; mt < NMAT; ++mt) {
-        const bf16x8 B0 = wstep_operand<FMT, NMAT>(st, mt, 2 * j);
-        const bf16x8 B1 = wstep_operand<FMT, NMAT>(st, mt, 2 * j + 1);
+      for (int j = 0; j < 4; ++j) {
+        const auto r = __builtin_amdgcn_permlane16_swap(wstep_dword(st, mt, 2 * j),
+                                                        wstep_dword(st, mt, 2 * j + 1), false,
+                                                        false);
+        dw[2 * j] = r[0];
+        dw[2 * j + 1] = r[1];
+      }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f32x4 ch = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, q0 == q ? B0 : Z,
-                                                              f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          ch = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, q0 == q ? B1 : Z, ch, 0, 0, 0);
+      for (int r = 0; r < 8; ++r) {
+        const bf16x8 B = fp4x8_to_bf16x8(dw[r], 1.0f);
+        // K offset of this lane's 8 values of dword r within the step
+        const int koff = 128 * (gl >> 1) + 64 * (r & 1) + 16 * (r >> 1) + 8 * (gl & 1);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mt][i] += (double)ch[i];
+        for (int half = 0; half < 2; ++half) {
+          const bf16x8 A = *(const bf16x8*)((gl >> 1) == half ? arow + koff : zrow);
+          const f32x4 part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              A, B, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          const double sc = (double)e4m3_f32(byte_of(st.s16[mt], 8 * half + 4 * (r & 1) + (r >> 1)));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mt][i] = fma((double)part[i], sc, acc[mt][i]);
         }
       }
-      // keeps the scheduler from dequantising many operands ahead (they spill)
+      // keeps the scheduler from converting many operands ahead (they spill)
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -486,7 +513,8 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
   const uint8_t** tw = (const uint8_t**)((char*)lds + tab_off);
   const uint8_t** ts = tw + a.E;
   float* tt = (float*)(ts + a.E);
-  // gate/up under W4A4: one tile's h, [16 tokens][64 rows] BF16
+  // gate/up under W4A4: one tile's h, [16 tokens][64 rows] BF16; E4M3: a
+  // 16-byte zero block (the A operand of the lanes whose group an MFMA skips)
   uint16_t* hl = (uint16_t*)((char*)lds + ((tab_off + a.E * (2 * (int)sizeof(void*) + 4) + 15) & ~15));
   const int npairs = a.T * a.K;
 
@@ -494,6 +522,7 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
   // The first 256 ids are requested with the expert tables, so that both
   // round trips overlap.
   const int id0 = tid < npairs ? a.ids[tid] : -1;
+  if (FMT == MOE_SCALE_E4M3_G16 && tid < 4) ((uint32_t*)hl)[tid] = 0u;
   for (int e = tid; e < a.E; e += 64 * kBW) {
     cnt[e] = 0;
     tw[e] = a.wtab[e];
@@ -652,9 +681,12 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
                           acc);
       }
     } else {
-      const uint16_t* arow = xs + ln * ldx + 64 * gl + st * KS * kKS;
+      // E8M0: the lane group's own K slice; E4M3: the step's start (the
+      // pair-swapped operands choose their slices themselves)
+      const uint16_t* arow =
+          xs + ln * ldx + (FMT == MOE_SCALE_E8M0_G32 ? 64 * gl : 0) + st * KS * kKS;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) wstep_mfma<FMT, NMAT>(W[ks], arow + ks * kKS, acc);
+      for (int ks = 0; ks < KS; ++ks) wstep_mfma<FMT, NMAT>(W[ks], arow + ks * kKS, hl, acc);
     }
     if (st != nst - 1) return;
     // epilogue: lane holds D[m = 4 gl + i][n] of the M tile
@@ -911,7 +943,8 @@ hipError_t launch_gemm_ks(const BatchedArgs& a, hipStream_t s) {
   const int Kd = MODE == 0 ? a.H : a.I;
   const size_t lds = (size_t)kMC * (Kd + 8) * 2 + (size_t)(kMC + 2 * a.E + 1 + kBW) * 4 + 8 +
                      (size_t)a.E * (2 * sizeof(void*) + sizeof(float)) +
-                     (MODE == 0 && A4 ? 16 + 1024 * 2 : 0);
+                     (MODE == 0 && A4 ? 16 + 1024 * 2 : 0) +
+                     (FMT == MOE_SCALE_E4M3_G16 ? 16 + 16 : 0);
   // The largest shape a check admits (K 4096, 1024 experts) needs 156.3 KiB,
   // 158.3 KiB for gate/up under W4A4.
   static size_t allowed = 0;  // benign race: the value only grows towards the same bound
