@@ -177,6 +177,27 @@ def decode_floor(args, store, stream, dev, xs, ids, rws, cfg, warmup, steps, buf
             M.moe_w4a16_empty_launch(256, 256, sink, stream)
 
     empty_step_ms = graph_ms(empty_step, steps)
+
+    # a grid-wide barrier inside one kernel (what a persistent kernel would
+    # pay per in-kernel dependency): one workgroup per CU, 0 and 200 barriers
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    ctr = torch.zeros(2, dtype=torch.int32, device=dev)
+    barrier_us = {}
+    for wg in (64, ncu):
+        t = {}
+        for nb in (0, 200):
+            ts = []
+            for _ in range(8):
+                ctr.zero_()
+                M.moe_w4a16_timing_begin(1)
+                M.moe_w4a16_grid_barrier(wg, nb, ctr, stream)
+                msl, _ = M.moe_w4a16_timing_end(1)
+                ts += msl
+            t[nb] = float(np.median(ts) * 1e3)
+        torch.cuda.synchronize()
+        if int(ctr[1].item()) != 0:
+            raise RuntimeError("grid barrier probe: a bounded poll gave up")
+        barrier_us[str(wg)] = (t[200] - t[0]) / 200
     burst = {}
     for kind, nb in (("1", 13373440), ("2", 6692864)):
         nreg = buf.numel() // nb
@@ -184,6 +205,7 @@ def decode_floor(args, store, stream, dev, xs, ids, rws, cfg, warmup, steps, buf
             buf.data_ptr() + (i % nreg) * nb, nb, lpl, sink, stream)) for lpl in (1, 2, 4, 8)}
     return {"loads_only_us": loads_only, "empty_us": empty, "burst_read_us": burst,
             "graph_loads_only_step_ms": floor_step_ms, "graph_empty_step_ms": empty_step_ms,
+            "grid_barrier_us_by_workgroups": barrier_us,
             "launches_per_step": 2 * L + 1,
             "burst_read_best_us": {k: min(v.values()) for k, v in burst.items()},
             "note": "kinds: 1 = decode gate/up (13,373,440 B per launch), 2 = decode down + "
@@ -671,8 +693,9 @@ def pmc_summary(args):
         cp_w, _ = per_kernel(write, "elementwise")
     f_fetch = gib_kib / max(v for n, v in fetch if "k_stream_read" in n)
     f_write = (256 * 1024.0) / max(v for n, v in write if ("copyBuffer" in n or "elementwise" in n))
-    names = {1: "k_dec_gateup", 2: "k_dec_down", 4: "k_bat_gemm<0, 0", 5: "k_bat_gemm<0, 1"}
     wl = os.environ.get("PMC_WORKLOAD", "c1")
+    fmt = 1 if wl.startswith("c4") else 0  # the E4M3 workloads' kernels carry FMT = 1
+    names = {1: "k_dec_gateup", 2: "k_dec_down", 4: f"k_bat_gemm<{fmt}, 0", 5: f"k_bat_gemm<{fmt}, 1"}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     for kind, pat in names.items():
         fk, nf = per_kernel(fetch, pat)

@@ -343,6 +343,14 @@ int moe_w4a16_stream_read(const void* src, size_t bytes, void* sink, void* strea
  *   aligned) with bytes / (16 * 256 * loads_per_lane) workgroups of 256
  *   lanes, each lane issuing all of its `loads_per_lane` (1, 2, 4 or 8)
  *   16-byte loads before it uses any; `sink` as above.
+ * moe_w4a16_grid_barrier: one kernel of `workgroups` (1 .. the device's CU
+ *   count, so that all are resident at once) single-wave workgroups that
+ *   pass `barriers` (0 .. 100000) grid-wide barriers: each workgroup adds 1
+ *   to counter[0] (relaxed, agent scope) and polls it until every workgroup
+ *   has arrived.  counter: device uint32 [2], zero on entry (counter[0] ends
+ *   at workgroups * barriers; counter[1] gets bit 0 if a bounded poll gave
+ *   up, so the kernel always ends).  Timing it with and without barriers
+ *   gives the cost of one in-kernel grid dependency.
  */
 int moe_w4a16_decode_floor(int32_t num_layers, const void* x, const int32_t* expert_ids,
                            const void* route_w, const void* const* packed_weights,
@@ -350,6 +358,7 @@ int moe_w4a16_decode_floor(int32_t num_layers, const void* x, const int32_t* exp
 int moe_w4a16_empty_launch(int32_t workgroups, int32_t threads, void* sink, void* stream);
 int moe_w4a16_read_burst(const void* src, size_t bytes, int32_t loads_per_lane, void* sink,
                          void* stream);
+int moe_w4a16_grid_barrier(int32_t workgroups, int32_t barriers, void* counter, void* stream);
 
 /* Measurement helper: one wave that spins for `microseconds` (at most
  * 1,000,000) on the 100 MHz real-time counter, so that a host can enqueue
@@ -376,6 +385,7 @@ int moe_w4a16_delay(uint32_t microseconds, void* stream);
 #define MOE_KERNEL_FLOOR_DOWN 16     /* moe_w4a16_decode_floor: decode down's loads only */
 #define MOE_KERNEL_EMPTY 17          /* moe_w4a16_empty_launch */
 #define MOE_KERNEL_READ_BURST 18     /* moe_w4a16_read_burst */
+#define MOE_KERNEL_GRID_BARRIER 19   /* moe_w4a16_grid_barrier */
 
 /*
  * Kernel timing (measurement only).  After moe_w4a16_timing_begin(capacity)

@@ -446,6 +446,20 @@ int moe_w4a16_empty_launch(int32_t workgroups, int32_t threads, void* sink, void
   return e == hipSuccess ? ok() : hip_fail(e, "empty launch");
 }
 
+int moe_w4a16_grid_barrier(int32_t workgroups, int32_t barriers, void* counter, void* stream) {
+  if (workgroups < 1 || barriers < 0 || barriers > 100000 || !counter || !aligned(counter, 4))
+    return fail(MOE_ERR_INVALID_ARG, "workgroups >= 1, barriers 0..100000, an aligned counter");
+  int dev = 0, ncu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "device attributes");
+  if (workgroups > ncu)
+    return fail(MOE_ERR_INVALID_ARG, "workgroups %d above the %d CUs: not all resident at once",
+                workgroups, ncu);
+  e = launch_grid_barrier(workgroups, barriers, (uint32_t*)counter, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "grid barrier launch");
+}
+
 int moe_w4a16_read_burst(const void* src, size_t bytes, int32_t loads_per_lane, void* sink,
                          void* stream) {
   if (!src || !sink) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");

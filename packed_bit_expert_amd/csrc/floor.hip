@@ -7,10 +7,12 @@
 // everything it loaded into one word with XOR, which it stores where its
 // decode kernel stores its results (h, out), so that the loads cannot be
 // dropped and the same stores complete before the kernel ends.  Next to
-// them: an empty kernel of a given grid (the launch alone), and a read of a
+// them: an empty kernel of a given grid (the launch alone), a read of a
 // byte range in which every lane issues all of its 16-byte loads before it
 // uses any (the cost of moving the same bytes with no dependent load in
-// front of them).
+// front of them), and a kernel of repeated grid-wide barriers (what a
+// persistent kernel would pay per in-kernel dependency instead of a kernel
+// boundary).
 //
 // The decode kernels they mirror are fixed to the LFM2.5-24B-A2B shape
 // (hidden 2048, expert intermediate 1536, top-4, E8M0 per 32): "LFM2.5-24B-A2B
@@ -103,6 +105,37 @@ __global__ __launch_bounds__(256) void k_floor_down(const SlotRef* pre, const ui
   if (tid < 8) out[m0 + tid] = (uint16_t)acc;
 }
 
+// `nbar` grid-wide barriers in one kernel: thread 0 of every workgroup adds 1
+// to a counter that starts at zero (relaxed, agent scope: the cheapest
+// arrival) and spins until it reaches (i + 1) * gridDim.x.  The grid must be
+// resident all at once (at most one workgroup per CU is launched).  Every
+// spin is bounded: past kSpinLimit polls the workgroup sets bit 0 of
+// counter[1] and returns, so the kernel ends whatever happens.
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+__global__ __launch_bounds__(64) void k_grid_barrier(uint32_t* counter, int nbar) {
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  for (int i = 0; i < nbar; ++i) {
+    if (threadIdx.x == 0) {
+      const uint32_t target = (uint32_t)(i + 1) * gridDim.x;
+      __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      uint32_t n = 0;
+      while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        if (++n > kSpinLimit) {
+          bad = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    __syncthreads();
+    if (bad) break;
+  }
+  if (threadIdx.x == 0 && bad) atomicOr(counter + 1, 1u);
+}
+
 __global__ void k_empty(uint32_t never, uint32_t* sink) {
   if (blockIdx.x == never) sink[0] = 1u;
 }
@@ -150,6 +183,11 @@ hipError_t launch_decode_floor(const SlotRef* pre, const uint16_t* x, uint16_t* 
 hipError_t launch_empty(int workgroups, int threads, uint32_t* sink, hipStream_t s) {
   return launch_kernel(MOE_KERNEL_EMPTY, k_empty, dim3(workgroups), dim3(threads), 0, s, kNever,
                        sink);
+}
+
+hipError_t launch_grid_barrier(int workgroups, int barriers, uint32_t* counter, hipStream_t s) {
+  return launch_kernel(MOE_KERNEL_GRID_BARRIER, k_grid_barrier, dim3(workgroups), dim3(64), 0, s,
+                       counter, barriers);
 }
 
 hipError_t launch_read_burst(const void* src, size_t bytes, int loads_per_lane, uint32_t* sink,

@@ -112,6 +112,7 @@ hipError_t launch_decode_floor(const SlotRef* pre, const uint16_t* x, uint16_t* 
                                const uint16_t* rw, const uint16_t* residual, uint16_t* out,
                                hipStream_t s);
 hipError_t launch_empty(int workgroups, int threads, uint32_t* sink, hipStream_t s);
+hipError_t launch_grid_barrier(int workgroups, int barriers, uint32_t* counter, hipStream_t s);
 hipError_t launch_read_burst(const void* src, size_t bytes, int loads_per_lane, uint32_t* sink,
                              hipStream_t s);
 bool router_supported(int H, int E, int K);

@@ -45,7 +45,7 @@ EXPORTS = [
     "moe_w4a16_stack_forward_routed", "moe_w4a16_hybrid_create", "moe_w4a16_hybrid_destroy",
     "moe_w4a16_hybrid_forward", "moe_w4a16_hybrid_stats", "moe_w4a16_hybrid_last_requests",
     "moe_w4a16_decode_floor", "moe_w4a16_empty_launch", "moe_w4a16_read_burst",
-    "moe_w4a16_forward_noalloc",
+    "moe_w4a16_forward_noalloc", "moe_w4a16_grid_barrier",
 ]
 
 
@@ -70,7 +70,8 @@ KERNEL_KINDS = {1: "decode gate/up", 2: "decode down + combine", 3: "slot resolv
                 8: "dequant", 9: "stream read", 10: "workspace fill", 11: "delay",
                 12: "router", 13: "pre-norm",
                 14: "x to MXFP4", 15: "decode gate/up floor (loads only)",
-                16: "decode down floor (loads only)", 17: "empty kernel", 18: "burst read"}
+                16: "decode down floor (loads only)", 17: "empty kernel", 18: "burst read",
+                19: "grid barriers"}
 
 
 class Dump(C.Structure):
@@ -107,6 +108,7 @@ def lib():
             "moe_w4a16_decode_floor": (C.c_int, [I32, P, P, P, P, P, P, C.POINTER(Cfg)]),
             "moe_w4a16_empty_launch": (C.c_int, [I32, I32, P, P]),
             "moe_w4a16_read_burst": (C.c_int, [P, SZ, I32, P, P]),
+            "moe_w4a16_grid_barrier": (C.c_int, [I32, I32, P, P]),
             "moe_w4a16_route": (C.c_int, [P, P, P, P, P, C.POINTER(Cfg)]),
             "moe_w4a16_forward_routed": (C.c_int, [P, P, P, P, P, P, P, P, C.POINTER(Cfg)]),
             "moe_w4a16_stack_forward_routed": (C.c_int, [I32, P, P, P, P, P, P, P, P, P,
@@ -271,6 +273,11 @@ def moe_w4a16_empty_launch(workgroups, threads, sink, stream=0):
 def moe_w4a16_read_burst(src, nbytes, loads_per_lane, sink, stream=0):
     _check(lib().moe_w4a16_read_burst(_p(src), nbytes, loads_per_lane, _p(sink),
                                       None if stream == 0 else _stream(stream)))
+
+
+def moe_w4a16_grid_barrier(workgroups, barriers, counter, stream=0):
+    _check(lib().moe_w4a16_grid_barrier(workgroups, barriers, _p(counter),
+                                        None if stream == 0 else _stream(stream)))
 
 
 def moe_w4a16_timing_begin(capacity: int):

@@ -223,6 +223,10 @@ def test_floor_helpers_reject_bad_arguments():
     with pytest.raises(M.MoeError) as e:
         M.moe_w4a16_read_burst(FAKE + 8, 4096, 4, FAKE)
     assert e.value.code == M.ERR_MISALIGNED
+    for args in ((0, 10, FAKE), (8, -1, FAKE), (8, 200000, FAKE), (8, 10, 0), (8, 10, FAKE + 2)):
+        with pytest.raises(M.MoeError) as e:
+            M.moe_w4a16_grid_barrier(*args)
+        assert e.value.code == M.ERR_INVALID_ARG, args
 
 
 def test_workspace_control_words_do_not_move_with_cfg():
