@@ -424,10 +424,14 @@ def measure(args, wkey, store, stream, dev, steps, warmup, cpu_seconds, calib=No
                 "plain_read_same_bytes_us": plain_us,
                 "frac_of_plain_read": plain_us / dominant["mean_us"] if plain_us else None}
         if floor is not None and dominant["_kind"] in (1, 2):
-            lo = floor["loads_only_us"][str(dominant["_kind"])]
+            # the step's floor: the same launches moving the same bytes with
+            # no arithmetic, replayed from a graph like the step itself (the
+            # event-timed single kernels carry a ~4 us timing floor that hides
+            # the difference; see floor["empty_us"])
             roof["floor"] = floor
-            roof["floor_us"] = lo
-            roof["frac_of_floor"] = lo / dominant["mean_us"]
+            roof["floor_step_ms"] = floor["graph_loads_only_step_ms"]
+            roof["frac_of_floor"] = floor["graph_loads_only_step_ms"] / ms_step
+            roof["launch_floor_step_ms"] = floor["graph_empty_step_ms"]
         if dominant["_kind"] in (4, 5):
             fl = kernel_flops(shape, T, dominant["_kind"])
             roof["mfma_useful_TFLOPs"] = fl / (dominant["mean_us"] / 1e6) / 1e12

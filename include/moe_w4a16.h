@@ -332,8 +332,9 @@ int moe_w4a16_stream_read(const void* src, size_t bytes, void* sink, void* strea
  *   issue the same loads in the same order -- the selected experts' nibbles
  *   and scales, x, h, the coefficients and the residual -- fold them with
  *   XOR (no dequantisation, no products, no reductions) and store the fold
- *   where the decode kernels store h (in the workspace) and out (here in
- *   `sink`).  Only the
+ *   where the decode kernels store h (in the workspace) and the layer output
+ *   (workspace buffers in turn, which the next layer reads as its input, as
+ *   in the stack; the last layer's in `sink`).  Only the
  *   LFM2.5-24B-A2B shape (hidden 2048, inter 1536, top-4) with E8M0 scales;
  *   otherwise MOE_ERR_UNSUPPORTED_SHAPE.
  * moe_w4a16_empty_launch: one kernel of `workgroups` x `threads` (1..1024)

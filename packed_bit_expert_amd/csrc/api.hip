@@ -427,14 +427,16 @@ int moe_w4a16_decode_floor(int32_t num_layers, const void* x, const int32_t* exp
           (int)E, lc.flags, err, slots, s);
       if (e != hipSuccess) return hip_fail(e, "slot resolve launch");
     }
-    // the layer input alternates between x and the workspace's ping buffer,
-    // as in the stack
+    // as in the stack, each layer reads what the previous layer's down
+    // kernel has just written: its output goes to one of two workspace
+    // buffers in turn (the last layer's to sink), and the next layer reads it
+    void* dst = l + 1 == num_layers ? sink : (void*)(ws + (l % 2 == 0 ? L.ping : L.scratch));
     hipError_t e = launch_decode_floor(slots + (size_t)g * T * K, (const uint16_t*)src,
                                        (uint16_t*)(ws + L.hbuf),
                                        (const uint16_t*)route_w + (size_t)l * T * K,
-                                       (const uint16_t*)src, (uint16_t*)sink, s);
+                                       (const uint16_t*)src, (uint16_t*)dst, s);
     if (e != hipSuccess) return hip_fail(e, "decode floor launch");
-    src = (l % 2 == 0) ? (const void*)(ws + L.ping) : x;
+    src = dst;
   }
   return ok();
 }
