@@ -190,76 +190,114 @@ __device__ __forceinline__ uint32_t byte_of(const uint4& v, int b) {
   return (w >> (8 * (b & 3))) & 255u;
 }
 
-// One K step: 8 MFMAs per matrix on one 16-token tile (E8M0; E4M3 below).  Each MFMA's FP32
-// result (32 exact BF16 products) is added to FP64 accumulators, which keeps
-// the BF16 outputs correctly rounded almost always (as in the decode path).
-// Chaining MFMAs in FP32 instead is cheaper but flips output roundings often
-// enough that the slot-order BF16 combine, where slots cancel, turns a flip
-// into an error above the 1% parity bound.
-// E8M0: arow = the lane's token row at its lane group's K slice of the step.
-// E4M3: arow = the lane's token row at the start of the step, and zrow a
-// 16-byte zero block in LDS.
-template <int FMT, int NMAT>
-__device__ __forceinline__ void wstep_mfma(const WStep<FMT, NMAT>& st, const uint16_t* arow,
-                                           const uint16_t* zrow, double (&acc)[2][4]) {
-  if constexpr (FMT == MOE_SCALE_E8M0_G32) {
+// One K step, E8M0: 8 MFMAs per matrix on one 16-token tile.  Each MFMA's
+// FP32 result (32 exact BF16 products) is added to FP64 accumulators, which
+// keeps the BF16 outputs correctly rounded almost always (as in the decode
+// path).  Chaining MFMAs in FP32 instead is cheaper but flips output
+// roundings often enough that the slot-order BF16 combine, where slots
+// cancel, turns a flip into an error above the 1% parity bound.
+// arow = the lane's token row at its lane group's K slice of the step.
+template <int NMAT>
+__device__ __forceinline__ void wstep_mfma(const WStep<MOE_SCALE_E8M0_G32, NMAT>& st,
+                                           const uint16_t* arow, double (&acc)[2][4]) {
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const bf16x8 A = *(const bf16x8*)(arow + 8 * d);
-#pragma unroll
-      for (int mt = 0; mt < NMAT; ++mt) {
-        const f32x4 part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            A, wstep_operand<FMT, NMAT>(st, mt, d), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mt][i] += (double)part[i];
-      }
-    }
-  } else {
-    // E4M3: the scale groups are 16 values and their scales differ by up to
-    // 2^14 within a row, so an FP32 sum across groups rounds often enough to
-    // break the parity bound where the slots cancel: every MFMA must sum one
-    // group only.  Lane group g loaded the step's groups 4g .. 4g + 3, group
-    // 4g + j in dwords 2j (its first 8 values) and 2j + 1 (its last 8).  One
-    // gfx950 permlane16 swap per pair of dwords exchanges the second dword of
-    // lane groups 0 and 2 with the first dword of lane groups 1 and 3, after
-    // which dword 2j holds group j in lane groups 0 | 1 (first | last 8
-    // values) and group 8 + j in lane groups 2 | 3, and dword 2j + 1 holds
-    // groups 4 + j and 12 + j the same way.  Each dword then feeds two
-    // MFMAs, one per group: the lane groups of the other group read a zero
-    // block as their A operand.  The codes go in unscaled (exact in BF16),
-    // each MFMA sums 16 products of one group in FP32, and its result is
-    // scaled by the group's E4M3 value in FP64 (exact product, one rounding
-    // in the add).
-    const int gl = (int)(threadIdx.x & 63) >> 4;  // this lane's group
+  for (int d = 0; d < 8; ++d) {
+    const bf16x8 A = *(const bf16x8*)(arow + 8 * d);
 #pragma unroll
     for (int mt = 0; mt < NMAT; ++mt) {
-      uint32_t dw[8];
+      const f32x4 part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          A, wstep_operand<MOE_SCALE_E8M0_G32, NMAT>(st, mt, d), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const auto r = __builtin_amdgcn_permlane16_swap(wstep_dword(st, mt, 2 * j),
-                                                        wstep_dword(st, mt, 2 * j + 1), false,
-                                                        false);
-        dw[2 * j] = r[0];
-        dw[2 * j + 1] = r[1];
-      }
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const bf16x8 B = fp4x8_to_bf16x8(dw[r], 1.0f);
-        // K offset of this lane's 8 values of dword r within the step
-        const int koff = 128 * (gl >> 1) + 64 * (r & 1) + 16 * (r >> 1) + 8 * (gl & 1);
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const bf16x8 A = *(const bf16x8*)((gl >> 1) == half ? arow + koff : zrow);
-          const f32x4 part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              A, B, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          const double sc = (double)e4m3_f32(byte_of(st.s16[mt], 8 * half + 4 * (r & 1) + (r >> 1)));
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mt][i] = fma((double)part[i], sc, acc[mt][i]);
-        }
-      }
-      // keeps the scheduler from converting many operands ahead (they spill)
-      __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 4; ++i) acc[mt][i] += (double)part[i];
     }
+  }
+}
+
+// One K step, E4M3.  The scale groups are 16 values and their scales differ
+// by up to 2^14 within a row, so an FP32 sum across groups rounds often
+// enough to break the parity bound where the slots cancel: every MFMA sums
+// one group per output.  Lane group g loaded the step's groups 4g .. 4g + 3,
+// group 4g + j in dwords 2j (its first 8 values) and 2j + 1 (its last 8).
+// One gfx950 permlane16 swap per pair of dwords exchanges the second dword
+// of lane groups 0 and 2 with the first dword of lane groups 1 and 3, after
+// which dword r holds group c(r) = 4 (r & 1) + (r >> 1) in lane groups 0 | 1
+// (first | last 8 values) and group c(r) + 8 in lane groups 2 | 3; the
+// lane's 8 values sit at K offset 128 (g >> 1) + 8 (g & 1) + 64 (r & 1) +
+// 16 (r >> 1) of the step.  The codes go in unscaled (exact in BF16), each
+// MFMA output sums 16 products of one group in FP32, and is scaled by the
+// group's E4M3 value in FP64 (exact product, one rounding in the add).
+//   DUAL = false (passes of 9..16 tokens): two MFMAs per dword, one per
+//     group; the lanes of the other group read zeros as their A operand.
+//     b0, b1: the A row of this lane for the MFMA of group c(r) | c(r) + 8
+//     (the zero block for lanes of the other group).
+//   DUAL = true (passes of at most 8 tokens): one MFMA per dword covers
+//     both groups, tokens 0..7 of group c(r) in output rows 0..7 and the
+//     same tokens of group c(r) + 8 in rows 8..15: lane (m, g) reads token
+//     m & 7 if m >> 3 == g >> 1, else zeros (b0), and output lane (n, g)
+//     accumulates group c(r) + 8 (g >> 1).  The two halves of the wave are
+//     added at the end of the tile.
+// The A operands are shared by both matrices.  b0, b1 are LDS byte
+// addresses; every per-dword offset is a constant.
+template <int NMAT, bool DUAL>
+__device__ __forceinline__ void wstep_mfma_e4m3(const WStep<MOE_SCALE_E4M3_G16, NMAT>& st,
+                                                const char* b0, const char* b1, bool upper,
+                                                double (&acc)[2][4]) {
+  uint32_t dw[NMAT][8];
+  uint32_t sp[NMAT][4];
+#pragma unroll
+  for (int mt = 0; mt < NMAT; ++mt) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const auto r = __builtin_amdgcn_permlane16_swap(wstep_dword(st, mt, 2 * j),
+                                                      wstep_dword(st, mt, 2 * j + 1), false, false);
+      dw[mt][2 * j] = r[0];
+      dw[mt][2 * j + 1] = r[1];
+    }
+    const uint4 s = st.s16[mt];  // scale bytes of groups 0..15
+    if constexpr (!DUAL) {
+      // sp[q] = groups (2q, 2q + 8, 2q + 1, 2q + 9): one conversion per dword
+      // gives the scales of both of its MFMAs
+      sp[mt][0] = (s.x & 0xFFu) | (s.z & 0xFFu) << 8 | (s.x & 0xFF00u) << 8 | (s.z & 0xFF00u) << 16;
+      sp[mt][1] = (s.x >> 16 & 0xFFu) | (s.z >> 16 & 0xFFu) << 8 | (s.x >> 24) << 16 | (s.z >> 24) << 24;
+      sp[mt][2] = (s.y & 0xFFu) | (s.w & 0xFFu) << 8 | (s.y & 0xFF00u) << 8 | (s.w & 0xFF00u) << 16;
+      sp[mt][3] = (s.y >> 16 & 0xFFu) | (s.w >> 16 & 0xFFu) << 8 | (s.y >> 24) << 16 | (s.w >> 24) << 24;
+    } else {
+      // this lane's groups: 0..7, or 8..15 in the upper half of the wave
+      sp[mt][0] = upper ? s.z : s.x;
+      sp[mt][1] = upper ? s.w : s.y;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int c = 4 * (r & 1) + (r >> 1);
+    const int off = 2 * (64 * (r & 1) + 16 * (r >> 1));
+    const bf16x8 A0 = *(const bf16x8*)(b0 + off);
+    bf16x8 A1;
+    if constexpr (!DUAL) A1 = *(const bf16x8*)(b1 + off);
+#pragma unroll
+    for (int mt = 0; mt < NMAT; ++mt) {
+      const bf16x8 B = fp4x8_to_bf16x8(dw[mt][r], 1.0f);
+      if constexpr (!DUAL) {
+        const uint32_t q = sp[mt][c >> 1];
+        const f32x2 sc = (c & 1) ? e4m3x2_f32<true>(q) : e4m3x2_f32<false>(q);  // c, c + 8
+        const f32x4 p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        const f32x4 p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        const double s0 = (double)sc[0], s1 = (double)sc[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][i] = fma((double)p0[i], s0, acc[mt][i]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][i] = fma((double)p1[i], s1, acc[mt][i]);
+      } else {
+        const uint32_t q = sp[mt][c >> 2];
+        const f32x2 sc = (c & 2) ? e4m3x2_f32<true>(q) : e4m3x2_f32<false>(q);
+        const double s0 = (double)sc[c & 1];
+        const f32x4 p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][i] = fma((double)p[i], s0, acc[mt][i]);
+      }
+    }
+    // keeps the scheduler from converting many operands ahead (they spill)
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -514,7 +552,7 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
   const uint8_t** ts = tw + a.E;
   float* tt = (float*)(ts + a.E);
   // gate/up under W4A4: one tile's h, [16 tokens][64 rows] BF16; E4M3: a
-  // 16-byte zero block (the A operand of the lanes whose group an MFMA skips)
+  // 256-byte zero block (the A operand of the lanes whose group an MFMA skips)
   uint16_t* hl = (uint16_t*)((char*)lds + ((tab_off + a.E * (2 * (int)sizeof(void*) + 4) + 15) & ~15));
   const int npairs = a.T * a.K;
 
@@ -522,7 +560,7 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
   // The first 256 ids are requested with the expert tables, so that both
   // round trips overlap.
   const int id0 = tid < npairs ? a.ids[tid] : -1;
-  if (FMT == MOE_SCALE_E4M3_G16 && tid < 4) ((uint32_t*)hl)[tid] = 0u;
+  if (FMT == MOE_SCALE_E4M3_G16 && tid < 64) ((uint32_t*)hl)[tid] = 0u;
   for (int e = tid; e < a.E; e += 64 * kBW) {
     cnt[e] = 0;
     tw[e] = a.wtab[e];
@@ -680,15 +718,39 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
         wstep_mfma4<NMAT>(W[ks], rb + kg * (kKS / 2) + 32 * gl, rb + Kd / 2 + kg * (kKS / 32) + 2 * gl,
                           acc);
       }
-    } else {
-      // E8M0: the lane group's own K slice; E4M3: the step's start (the
-      // pair-swapped operands choose their slices themselves)
-      const uint16_t* arow =
-          xs + ln * ldx + (FMT == MOE_SCALE_E8M0_G32 ? 64 * gl : 0) + st * KS * kKS;
+    } else if constexpr (FMT == MOE_SCALE_E8M0_G32) {
+      // the lane group's own K slice of each step
+      const uint16_t* arow = xs + ln * ldx + 64 * gl + st * KS * kKS;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) wstep_mfma<FMT, NMAT>(W[ks], arow + ks * kKS, hl, acc);
+      for (int ks = 0; ks < KS; ++ks) wstep_mfma<NMAT>(W[ks], arow + ks * kKS, acc);
+    } else {
+      // the lane's K slice of the pair-swapped layout, and the zero block
+      const char* zb = (const char*)hl;
+      const int lanek = 128 * (gl >> 1) + 8 * (gl & 1) + st * KS * kKS;
+      const bool upper = gl >> 1;
+      if (it.mcnt <= 8) {
+        const bool mine = (ln >> 3) == (gl >> 1);
+        const char* ar = (const char*)(xs + (ln & 7) * ldx + lanek);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          wstep_mfma_e4m3<NMAT, true>(W[ks], mine ? ar + 2 * ks * kKS : zb, zb, upper, acc);
+      } else {
+        const char* ar = (const char*)(xs + ln * ldx + lanek);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          wstep_mfma_e4m3<NMAT, false>(W[ks], upper ? zb : ar + 2 * ks * kKS,
+                                       upper ? ar + 2 * ks * kKS : zb, upper, acc);
+      }
     }
     if (st != nst - 1) return;
+    if constexpr (FMT == MOE_SCALE_E4M3_G16) {
+      if (it.mcnt <= 8) {  // the two halves of the wave hold the same outputs' group halves
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mt][i] += xor_lane<32>(acc[mt][i], lane);
+      }
+    }
     // epilogue: lane holds D[m = 4 gl + i][n] of the M tile
     const int n = (tile % ntiles) * kBN + wave * 16 + ln;
     if constexpr (MODE == 0 && A4) lds_barrier();  // wave 0 has read the last tile's h
@@ -944,9 +1006,9 @@ hipError_t launch_gemm_ks(const BatchedArgs& a, hipStream_t s) {
   const size_t lds = (size_t)kMC * (Kd + 8) * 2 + (size_t)(kMC + 2 * a.E + 1 + kBW) * 4 + 8 +
                      (size_t)a.E * (2 * sizeof(void*) + sizeof(float)) +
                      (MODE == 0 && A4 ? 16 + 1024 * 2 : 0) +
-                     (FMT == MOE_SCALE_E4M3_G16 ? 16 + 16 : 0);
+                     (FMT == MOE_SCALE_E4M3_G16 ? 16 + 256 : 0);
   // The largest shape a check admits (K 4096, 1024 experts) needs 156.3 KiB,
-  // 158.3 KiB for gate/up under W4A4.
+  // 156.6 KiB with E4M3 scales, 158.3 KiB for gate/up under W4A4.
   static size_t allowed = 0;  // benign race: the value only grows towards the same bound
   if (lds > allowed) {
     hipError_t e = allow_lds(k_bat_gemm<FMT, MODE, KS, A4>, lds);
