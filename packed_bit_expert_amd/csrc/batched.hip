@@ -114,6 +114,10 @@ constexpr int kMC = 16;       // tokens per LDS pass
 // persistent workgroups per CU (gate/up, down): down's smaller token rows and
 // K-stages let three share a CU, which keeps more of its loads in flight
 constexpr int kWgPerCu[2] = {2, 3};
+// E4M3 tile costs for the split over CUs: tiles of passes of more than
+// kMC / 2 tokens (one scale group per MFMA) against the others (two)
+constexpr int kHeavy = 7, kLight = 4;
+__host__ __device__ constexpr int heavy_passes(int c) { return c / kMC + (c % kMC > kMC / 2 ? 1 : 0); }
 
 template <int FMT, int NMAT>
 struct WStep {
@@ -546,6 +550,7 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
   int* cnt = list + kMC;                // [E]
   int* pre = cnt + a.E;                 // [E + 1]: passes of the experts before e
   int* wcnt = pre + a.E + 1;            // [kBW]
+  __shared__ int cut[2];                // E4M3: this CU's first tile and the next CU's
   // the expert tables, staged once: weight bases, scale bases, tensor scales
   const int tab_off = (kMC * ldx * 2 + (kMC + 2 * a.E + 1 + kBW) * 4 + 7) & ~7;  // bytes
   const uint8_t** tw = (const uint8_t**)((char*)lds + tab_off);
@@ -605,6 +610,54 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
       }
     }
     if (lane == 63) pre[a.E] = incl;
+    if constexpr (FMT == MOE_SCALE_E4M3_G16) {
+      // E4M3: a tile of a pass of more than kMC / 2 tokens runs twice the
+      // MFMAs and about 1.75 times the VALU work of a smaller pass's tile
+      // (one scale group per MFMA instead of two), so the CUs get equal
+      // shares of cost kHeavy per such tile and kLight per other tile
+      // rather than equal tile counts.  An expert's heavy passes (all of
+      // its full passes, and the last one if it has more than kMC / 2
+      // tokens) come first, so the cost of its first j tiles is piecewise
+      // linear.  Lane l finds the first tile at or after each bound that
+      // falls in its experts' cost range.
+      int cmine = 0;
+      for (int i = 0; i < per; ++i) {
+        const int e = lane * per + i;
+        if (e < a.E) cmine += kLight * ((cnt[e] + kMC - 1) / kMC) + (kHeavy - kLight) * heavy_passes(cnt[e]);
+      }
+      long long cincl = cmine;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const long long v = __shfl_up(cincl, o);
+        if (lane >= o) cincl += v;
+      }
+      const long long W = __shfl(cincl, 63) * ntiles;
+      const int cu = (int)blockIdx.x % a.ncu;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const long long B = W * (cu + k) / a.ncu;
+        if (B >= W) {
+          if (lane == 0) cut[k] = pre[a.E] * ntiles;
+          continue;
+        }
+        long long C = (cincl - cmine) * ntiles;
+        if (B < C || B >= cincl * ntiles) continue;
+        for (int i = 0; i < per; ++i) {
+          const int e = lane * per + i;
+          if (e >= a.E) break;
+          const int hn = heavy_passes(cnt[e]) * ntiles;
+          const long long ce = (long long)kLight * ((cnt[e] + kMC - 1) / kMC) * ntiles + (long long)(kHeavy - kLight) * hn;
+          if (B < C + ce) {
+            const long long off = B - C;
+            const long long j = off <= (long long)kHeavy * hn ? (off + kHeavy - 1) / kHeavy
+                                                              : hn + (off - (long long)kHeavy * hn + kLight - 1) / kLight;
+            cut[k] = pre[e] * ntiles + (int)j;
+            break;
+          }
+          C += ce;
+        }
+      }
+    }
   }
   __syncthreads();
   // Tiles per CU, then per workgroup of the CU.  The grid is P workgroups
@@ -619,7 +672,8 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
   const int ncu = a.ncu, P = (int)gridDim.x / ncu;
   const int cu = (int)blockIdx.x % ncu, rank = (int)blockIdx.x / ncu;
   if (rank >= P) return;
-  const int cu0 = (int)(ntot * cu / ncu), ncut = (int)(ntot * (cu + 1) / ncu) - cu0;
+  const int cu0 = FMT == MOE_SCALE_E4M3_G16 ? cut[0] : (int)(ntot * cu / ncu);
+  const int ncut = (FMT == MOE_SCALE_E4M3_G16 ? cut[1] : (int)(ntot * (cu + 1) / ncu)) - cu0;
   int t0 = cu0;
   for (int q = 0; q < rank; ++q) t0 += (ncut + P - 1 - q) / P;
   const int t1 = t0 + (ncut + P - 1 - rank) / P;
