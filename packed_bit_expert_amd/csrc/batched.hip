@@ -126,18 +126,35 @@ struct WStep {
   uint4 s16[FMT == MOE_SCALE_E4M3_G16 ? NMAT : 1];  // E4M3: the row's 16 scale bytes of the step
 };
 
-// E8M0 scales of one stage, 8 bytes (one K step of a row) per step, loaded 16
-// bytes at a time: a scale load is as costly to issue as a weight load, so
-// one 16-byte load per two K steps instead of one 2-byte load per step.
+// The scales of one stage, loaded 16 bytes at a time: a scale load is as
+// costly to issue as a weight load.  E8M0: 8 bytes (one K step of a row) per
+// step, one 16-byte load per two K steps instead of one 2-byte load per
+// step.  E4M3: 16 bytes per step; of each pair of steps the even lane groups
+// load the first and the odd ones the second, and one permlane16 swap per
+// dword gives every lane both (see stage_scales_e4m3).
 template <int FMT, int NMAT, int KS>
 struct StageScales {
-  uint32_t q[NMAT][FMT == MOE_SCALE_E8M0_G32 ? 2 * KS : 1];
+  uint32_t q[NMAT][FMT == MOE_SCALE_E8M0_G32 ? 2 * KS : 4 * ((KS + 1) / 2)];
 };
 
 template <int FMT, int NMAT, int KS>
 __device__ __forceinline__ void load_stage_scales(StageScales<FMT, NMAT, KS>& ss,
-                                                  const uint8_t* const (&srow)[2], int st, bool ok) {
-  if constexpr (FMT == MOE_SCALE_E8M0_G32) {
+                                                  const uint8_t* const (&srow)[2], int st, int g,
+                                                  bool ok) {
+  if constexpr (FMT == MOE_SCALE_E4M3_G16) {
+#pragma unroll
+    for (int mt = 0; mt < NMAT; ++mt) {
+#pragma unroll
+      for (int p = 0; p < (KS + 1) / 2; ++p) {
+        const int step = st * KS + 2 * p + ((g & 1) && 2 * p + 1 < KS ? 1 : 0);
+        const uint4 v = ldg16(srow[mt] + (ok ? step * (kKS / 16) : 0));
+        ss.q[mt][4 * p] = v.x;
+        ss.q[mt][4 * p + 1] = v.y;
+        ss.q[mt][4 * p + 2] = v.z;
+        ss.q[mt][4 * p + 3] = v.w;
+      }
+    }
+  } else {
 #pragma unroll
     for (int mt = 0; mt < NMAT; ++mt) {
 #pragma unroll
@@ -157,19 +174,42 @@ __device__ __forceinline__ void load_stage_scales(StageScales<FMT, NMAT, KS>& ss
   }
 }
 
-// K step ks of this lane's rows (E4M3 scales with it).  A rejected expert
+// E4M3: every step's 16 scale bytes in every lane.  permlane16_swap(v, v)
+// swaps lane groups 1 and 3 of its first result with lane groups 0 and 2 of
+// its second, so the first result holds, in every lane group, what the even
+// lane groups loaded (step 2p) and the second what the odd ones loaded
+// (step 2p + 1).  A last unpaired step was loaded by every lane group.
+template <int NMAT, int KS>
+__device__ __forceinline__ void stage_scales_e4m3(const StageScales<MOE_SCALE_E4M3_G16, NMAT, KS>& ss,
+                                                  WStep<MOE_SCALE_E4M3_G16, NMAT> (&W)[KS]) {
+#pragma unroll
+  for (int mt = 0; mt < NMAT; ++mt) {
+#pragma unroll
+    for (int p = 0; p < (KS + 1) / 2; ++p) {
+      if (2 * p + 1 < KS) {
+        uint32_t ev[4], od[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const auto r = __builtin_amdgcn_permlane16_swap(ss.q[mt][4 * p + d], ss.q[mt][4 * p + d], false, false);
+          ev[d] = r[0];
+          od[d] = r[1];
+        }
+        W[2 * p].s16[mt] = make_uint4(ev[0], ev[1], ev[2], ev[3]);
+        W[2 * p + 1].s16[mt] = make_uint4(od[0], od[1], od[2], od[3]);
+      } else {
+        W[2 * p].s16[mt] = make_uint4(ss.q[mt][4 * p], ss.q[mt][4 * p + 1], ss.q[mt][4 * p + 2], ss.q[mt][4 * p + 3]);
+      }
+    }
+  }
+}
+
+// K step ks of this lane's rows.  A rejected expert
 // (ok = false) reads the same first bytes of a harmless valid buffer instead.
 template <int FMT, int NMAT>
 __device__ __forceinline__ void load_wstep(WStep<FMT, NMAT>& st, const uint8_t* const (&wrow)[2],
                                            const uint8_t* const (&srow)[2], int ks, int g,
                                            bool ok) {
   const int wo = ok ? ks * (kKS / 2) + 32 * g : 0;
-  if constexpr (FMT == MOE_SCALE_E4M3_G16) {
-    // all 16 scale groups of the row's step: after the pair swap below a
-    // lane accumulates MFMA results of every group of its row
-#pragma unroll
-    for (int mt = 0; mt < NMAT; ++mt) st.s16[mt] = ldg16(srow[mt] + (ok ? ks * (kKS / 16) : 0));
-  }
 #pragma unroll
   for (int mt = 0; mt < NMAT; ++mt) {
     const uint8_t* src = wrow[mt] + wo;
@@ -538,7 +578,7 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
   constexpr int NMAT = MODE == 0 ? 2 : 1;
   constexpr int G = FMT == MOE_SCALE_E4M3_G16 ? 16 : 32;
   // vector loads of one stage, per lane
-  constexpr int NLOADS = FMT == MOE_SCALE_E8M0_G32 ? (2 * KS + (KS + 1) / 2) * NMAT : 3 * KS * NMAT;
+  constexpr int NLOADS = (2 * KS + (KS + 1) / 2) * NMAT;
   const int Kd = MODE == 0 ? a.H : a.I;
   const int Nd = MODE == 0 ? a.I : a.H;
   const int ntiles = Nd / kBN, nst = Kd / (kKS * KS);
@@ -727,7 +767,7 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
       isc = iok ? ts[e] : (const uint8_t*)a.x;
     }
     rows_for(tile % ntiles);
-    load_stage_scales<FMT, NMAT, KS>(SQ, srow, st, iok);
+    load_stage_scales<FMT, NMAT, KS>(SQ, srow, st, gl, iok);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) load_wstep<FMT, NMAT>(W[ks], wrow, srow, st * KS + ks, gl, iok);
   };
@@ -763,6 +803,8 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
 #pragma unroll
         for (int mt = 0; mt < NMAT; ++mt)
           W[ks].s[mt] = ((gl >> 1) ? SQ.q[mt][2 * ks + 1] : SQ.q[mt][2 * ks]) >> (16 * (gl & 1)) & 0xFFFFu;
+    } else {
+      stage_scales_e4m3<NMAT, KS>(SQ, W);
     }
     if constexpr (A4) {
       const uint8_t* rb = (const uint8_t*)(xs + ln * ldx);

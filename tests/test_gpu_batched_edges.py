@@ -130,3 +130,57 @@ def test_every_token_the_same_experts(layer_mx):
     GH.compare(out, layer_mx.oracle(x, ids, rw), "same experts")
     again, _ = layer_mx.gpu(x, ids, rw)
     assert np.array_equal(out, again)
+
+
+def _routing_with_counts(counts, T, K, E, filler_from):
+    """ids [T, K] in which expert e is routed exactly counts[e] times, every
+    token to K distinct experts; slots left over go to single-use experts
+    numbered from filler_from."""
+    ids = -np.ones((T, K), np.int32)
+    for e, c in sorted(counts.items(), key=lambda kv: -kv[1]):
+        free = sorted(range(T), key=lambda t: -int(np.sum(ids[t] < 0)))
+        n = 0
+        for t in free:
+            if n == c:
+                break
+            if e in ids[t] or not np.any(ids[t] < 0):
+                continue
+            ids[t, int(np.argmax(ids[t] < 0))] = e
+            n += 1
+        assert n == c, "the construction must place every pair"
+    nxt = filler_from
+    for t in range(T):
+        for j in range(K):
+            if ids[t, j] < 0:
+                ids[t, j] = nxt
+                nxt += 1
+    assert nxt <= E
+    return ids
+
+
+@pytest.fixture(scope="module")
+def layer_nv():
+    banner("upload LFM 2048/1536 E4M3 layer 2")
+    return GH.Layer(LFM, S.FMT_E4M3_G16, 2)
+
+
+def test_e4m3_pass_size_boundaries(layer_nv):
+    """E4M3 passes of at most 8 tokens put two scale groups in one MFMA and
+    larger passes one, and the tiles are split over the CUs by that cost:
+    experts routed 8, 9, 16, 17, 24 and 25 times give passes of 8 | 9 | 16 |
+    16 + 1 | 16 + 8 | 16 + 9 tokens next to single-token experts."""
+    T, K = 25, LFM.top_k
+    counts = {3: 25, 11: 24, 20: 17, 31: 16, 40: 9, 47: 8}
+    ids = _routing_with_counts(counts, T, K, LFM.experts, 48)
+    got = np.bincount(ids.ravel(), minlength=LFM.experts)
+    assert all(got[e] == c for e, c in counts.items())
+    assert all(len(set(row)) == K for row in ids.tolist())
+    banner(f"E4M3 T={T}, expert counts {sorted(counts.values())} + singletons")
+    x = S.activations(10, 2, 0, T, LFM.hidden)
+    _, rw = S.routing_uniform(10, 2, 0, T, LFM.experts, K)
+    r = S.activations(11, 2, 0, T, LFM.hidden)
+    out, st = layer_nv.gpu(x, ids, rw, residual=r)
+    assert st == 0
+    GH.compare(out, layer_nv.oracle(x, ids, rw, residual=r), "E4M3 pass-size boundaries")
+    again, _ = layer_nv.gpu(x, ids, rw, residual=r)
+    assert np.array_equal(out, again)
