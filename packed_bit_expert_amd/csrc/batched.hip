@@ -600,6 +600,10 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
   // 256-byte zero block (the A operand of the lanes whose group an MFMA skips)
   uint16_t* hl = (uint16_t*)((char*)lds + ((tab_off + a.E * (2 * (int)sizeof(void*) + 4) + 15) & ~15));
   const int npairs = a.T * a.K;
+  // this workgroup's CU and its rank among the CU's workgroups (scalars:
+  // computed once, ahead of any wave-dependent branch)
+  const int ncu = a.ncu, P = (int)gridDim.x / ncu;
+  const int cu = (int)blockIdx.x % ncu, rank = (int)blockIdx.x / ncu;
 
   // 1. the items: per-expert pair counts, then the prefix of their passes.
   // The first 256 ids are requested with the expert tables, so that both
@@ -672,10 +676,9 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
         if (lane >= o) cincl += v;
       }
       const long long W = __shfl(cincl, 63) * ntiles;
-      const int cu = (int)blockIdx.x % a.ncu;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        const long long B = W * (cu + k) / a.ncu;
+        const long long B = W * (cu + k) / ncu;
         if (B >= W) {
           if (lane == 0) cut[k] = pre[a.E] * ntiles;
           continue;
@@ -709,11 +712,11 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
   // the two workgroups of a CU equal counts, so CUs carried 2 or 4 tiles
   // at c2 where 3 or 4 suffice.
   const long long ntot = (long long)pre[a.E] * ntiles;
-  const int ncu = a.ncu, P = (int)gridDim.x / ncu;
-  const int cu = (int)blockIdx.x % ncu, rank = (int)blockIdx.x / ncu;
   if (rank >= P) return;
-  const int cu0 = FMT == MOE_SCALE_E4M3_G16 ? cut[0] : (int)(ntot * cu / ncu);
-  const int ncut = (FMT == MOE_SCALE_E4M3_G16 ? cut[1] : (int)(ntot * (cu + 1) / ncu)) - cu0;
+  // (the cut points come from LDS: read them as wave-uniform scalars, or the
+  // loop's tile and stage arithmetic would all run on the VALU)
+  const int cu0 = FMT == MOE_SCALE_E4M3_G16 ? __builtin_amdgcn_readfirstlane(cut[0]) : (int)(ntot * cu / ncu);
+  const int ncut = (FMT == MOE_SCALE_E4M3_G16 ? __builtin_amdgcn_readfirstlane(cut[1]) : (int)(ntot * (cu + 1) / ncu)) - cu0;
   int t0 = cu0;
   for (int q = 0; q < rank; ++q) t0 += (ncut + P - 1 - q) / P;
   const int t1 = t0 + (ncut + P - 1 - rank) / P;
