@@ -353,11 +353,14 @@ static int moe_forward_impl(int T, int H, int I, int E, int K, int fmt,
     if (a4 && (fmt != ORC_FMT_E8M0_G32 || H % 32 || I % 32)) return -1;
     for (int p = 0; p < T * K; ++p)
         if (ids[p] < 0 || ids[p] >= E) return -1;
+    /* the thread count applies to this call only (no process-wide setting) */
 #ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
+    const int nth = nthreads > 0 ? nthreads : omp_get_max_threads();
 #else
+    const int nth = 1;
     (void)nthreads;
 #endif
+    (void)nth;
     const size_t gate_n = 0, up_n = (size_t)I * H / 2, down_n = (size_t)I * H;  /* bytes */
     const size_t gate_s = 0, up_s = (size_t)I * H / G, down_s = 2 * (size_t)I * H / G;
 
@@ -380,7 +383,7 @@ static int moe_forward_impl(int T, int H, int I, int E, int K, int fmt,
         if (dump_u) memcpy(dump_u + (size_t)t * H, ub, sizeof(uint16_t) * (size_t)H);
 
         /* gate, up, silu*up for every slot */
-#pragma omp parallel for collapse(2) schedule(static)
+#pragma omp parallel for collapse(2) schedule(static) num_threads(nth)
         for (int j = 0; j < K; ++j)
             for (int n = 0; n < I; ++n) {
                 int e = ids[(size_t)t * K + j];
@@ -400,7 +403,7 @@ static int moe_forward_impl(int T, int H, int I, int E, int K, int fmt,
         if (a4)
             for (int j = 0; j < K; ++j) quant_row_values(hb + (size_t)j * I, I, hv + (size_t)j * I);
         /* down */
-#pragma omp parallel for collapse(2) schedule(static)
+#pragma omp parallel for collapse(2) schedule(static) num_threads(nth)
         for (int j = 0; j < K; ++j)
             for (int m = 0; m < H; ++m) {
                 int e = ids[(size_t)t * K + j];

@@ -94,3 +94,22 @@ def test_traffic_needs_the_current_source(tmp_path, monkeypatch):
         fh.write("\n// changed\n")
     assert bench.traffic_for(1, "c1") is None  # the kernel changed since
     assert bench.traffic_for(3, "c1") is None  # no summary kind for the slot resolve
+
+
+def test_cpu_baseline_thread_count_is_per_call():
+    """The bench times the oracle on every host core and then on one; the
+    one-thread run must not leave the process at one thread, or a later
+    all-cores baseline (the batch-32 sub-record's) runs on one core."""
+    import numpy as np
+
+    from oracle import oracle as O
+    sh = S.Shape(hidden=256, inter=128, experts=8, top_k=2, layers=1)
+    x = S.activations(1, 0, 0, 3, sh.hidden)
+    ids, rw = S.routing_uniform(1, 0, 0, 3, sh.experts, sh.top_k)
+    nib = [S.expert_nibbles(sh, S.FMT_E8M0_G32, 0, e) for e in range(sh.experts)]
+    sc = [S.expert_scales(sh, S.FMT_E8M0_G32, 0, e) for e in range(sh.experts)]
+    before = O.threads_available()
+    kw = dict(hidden=sh.hidden, inter=sh.inter, num_experts=sh.experts, fmt=S.FMT_E8M0_G32)
+    one = O.moe_forward(x, ids, rw, nib, sc, nthreads=1, **kw)
+    assert O.threads_available() == before
+    assert np.array_equal(one, O.moe_forward(x, ids, rw, nib, sc, **kw))
