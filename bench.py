@@ -417,7 +417,9 @@ def measure(args, wkey, store, stream, dev, steps, warmup, cpu_seconds, calib=No
     if dominant is not None and "achieved_GBps" in dominant:
         roof = {"bound": "hbm", "achieved": dominant["achieved_GBps"], "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": dominant["achieved_GBps"] / HBM_PEAK_GBPS,
-                "traffic": traffic_for(dominant["_kind"], base_workload(wkey)),
+                # counters of this exact workload only: the serial, routed, stacked
+                # and W4A4 variants launch other kernels or other byte counts
+                "traffic": traffic_for(dominant["_kind"], wkey),
                 "kernel": dominant["kernel"],
                 "alg_bytes_per_launch": dominant["alg_bytes_per_launch"],
                 "mean_launch_us": dominant["mean_us"],
