@@ -338,3 +338,31 @@ def test_serial_check_ids(layer_mx):
     s_out, s_st = layer_mx.gpu(x, bad, rw, flags=M.FLAG_CHECK_IDS | M.FLAG_SERIAL)
     assert g_st == s_st == 1
     assert np.array_equal(g_out, s_out)
+
+
+def test_e4m3_every_scale_code_through_both_paths():
+    """Every finite E4M3FN scale code, subnormals, zeros and negative codes
+    included, at random positions of every selected expert's scales, through
+    the decode kernels (T = 1) and the batched kernels (T = 32, Zipf routing:
+    passes on both sides of the two-groups-per-MFMA limit).  The device
+    decodes E4M3 with the gfx950 OCP FP8 conversion in several lane
+    positions (the dequant test covers one); the oracle decodes the format
+    from its definition."""
+    banner("E4M3: every finite scale code in every expert used, T=1 and T=32")
+    L = GH.Layer(LFM, S.FMT_E4M3_G16, 6)
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    rng = np.random.default_rng(7)
+    x1, ids1, rw1 = S.inputs(S.WORKLOADS["c4"], 0, 3)
+    x32, ids32, rw32 = S.inputs(S.WORKLOADS["c4b32"], 0, 3)
+    used = sorted({int(e) for e in np.concatenate([ids1.ravel(), ids32.ravel()])})
+    nb = L.store.nib_bytes
+    for e in used:
+        nib, sc = L.host(e)
+        sc = rng.choice(codes, size=sc.size).astype(np.uint8)
+        L._host[e] = (nib, sc)
+        L.store.buf[0, e, nb:].copy_(torch.from_numpy(sc))
+    torch.cuda.synchronize()
+    for x, ids, rw, what in ((x1, ids1, rw1, "T=1"), (x32, ids32, rw32, "T=32")):
+        out, st = L.gpu(x, ids, rw)
+        assert st == 0
+        GH.compare(out, L.oracle(x, ids, rw), f"E4M3 every code {what}")
