@@ -144,11 +144,11 @@ __global__ __launch_bounds__(256) void k_resolve(const int32_t* ids, const uint8
 // pre-norm once (FP64) for its four waves.  A rejected slot reads a harmless
 // valid address and writes zeros, so the code after the loads is
 // straight-line and each chunk waits only for its own load.
-template <int H, int FMT, bool PRENORM, bool DUMP>
+template <int H, int I, int FMT, bool PRENORM, bool DUMP>
 __global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
   // every argument the first loads depend on, fetched in one scalar batch
   // (the compiler would otherwise fetch them in dependent rounds near use)
-  asm volatile("" ::"s"(a.x), "s"(a.pre), "s"(a.slots), "s"(a.hbuf), "s"(a.T), "s"(a.I),
+  asm volatile("" ::"s"(a.x), "s"(a.pre), "s"(a.slots), "s"(a.hbuf), "s"(a.T), "s"(a.kmagic),
                "s"(a.K), "s"(a.eps));
   using S = GuShape<H>;
   using M = typename S::M;
@@ -156,15 +156,17 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
   constexpr int G = group_of<FMT>();
   __shared__ __attribute__((aligned(16))) uint16_t xs[PRENORM ? H : 8];
   __shared__ double red[4];
-  const int I = a.I;
-  const int per_slot = (I + RW - 1) / RW;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // The wave's slot and token, in scalar registers and without a division
+  // by a run-time value: these indices stand in front of the first load.
+  constexpr int per_slot = (I + RW - 1) / RW;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int gw = blockIdx.x * 4 + wave;
   // all waves of a workgroup belong to one token (per_slot * K is a multiple of 4)
   const int nb = gw % per_slot, sj = gw / per_slot;
   const bool live = sj < a.T * a.K;
   const int sjc = live ? sj : a.T * a.K - 1;
-  const int t = sjc / a.K, j = sjc - t * a.K;
+  const int t = (int)(((uint64_t)(uint32_t)sjc * a.kmagic) >> 32), j = sjc - t * a.K;
 
   // 0. the slot's expert (one 32-byte load of the pre-resolved table; without
   // one the load reads the workspace table, a harmless valid address, and
@@ -316,7 +318,8 @@ __global__ __launch_bounds__(256) void k_dec_down(DecodeArgs a) {
   const int nblk = H / ROWS;
   const int mb = blockIdx.x % nblk, t = blockIdx.x / nblk;
   const int m0 = mb * ROWS;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // a scalar: the slot indices
   const int li = lane % LPR, q = lane / LPR;
   const SlotRef* slots = a.pre ? a.pre : a.slots;
 
@@ -412,12 +415,18 @@ __global__ __launch_bounds__(256) void k_dec_down(DecodeArgs a) {
 }
 
 template <int H, int I, int FMT, bool PRENORM, bool DUMP>
-hipError_t launch_variant(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_variant(const DecodeArgs& a0, hipStream_t s) {
   // the pre-norm is shared by the four waves of a workgroup: they must belong
   // to one token
-  if (PRENORM && ((I / GuShape<H>::RW) * a.K) % 4 != 0) return hipErrorInvalidValue;
+  if (PRENORM && ((I / GuShape<H>::RW) * a0.K) % 4 != 0) return hipErrorInvalidValue;
+  if (a0.I != I || a0.H != H || a0.K < 1) return hipErrorInvalidValue;
+  DecodeArgs a = a0;
+  // floor(s / K) = (s * kmagic) >> 32 for every slot index s < 2^29 (kmagic =
+  // floor(2^32 / K) + 1 = (2^32 + e) / K with 0 < e <= K, so the product
+  // exceeds s / K by less than s * K / (K 2^32) < 1 / K)
+  a.kmagic = (uint64_t)((1ull << 32) / (uint64_t)a.K) + 1;
   const int waves = a.T * a.K * ((I + GuShape<H>::RW - 1) / GuShape<H>::RW);
-  const hipError_t e = launch_kernel(MOE_KERNEL_DECODE_GATE_UP, k_dec_gateup<H, FMT, PRENORM, DUMP>,
+  const hipError_t e = launch_kernel(MOE_KERNEL_DECODE_GATE_UP, k_dec_gateup<H, I, FMT, PRENORM, DUMP>,
                                      dim3((waves + 3) / 4), dim3(256), 0, s, a);
   if (e != hipSuccess) return e;
   return launch_kernel(MOE_KERNEL_DECODE_DOWN, k_dec_down<H, I, FMT, DUMP>,

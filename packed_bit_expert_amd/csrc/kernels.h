@@ -51,6 +51,7 @@ struct DecodeArgs {
   int T, H, I, K, E;
   uint32_t flags;
   float eps;
+  uint64_t kmagic;            // floor(2^32 / K) + 1, set by the decode launcher
 };
 
 // Arguments of the sorted batched path.
