@@ -2,7 +2,11 @@
 
 Every HIP source is compiled with packed-FP32 instruction selection turned
 off (``-packed-fp32-ops``): the kernels are written in scalar FP32 and must
-not be turned into v_pk_{add,mul,fma}_f32.
+not be turned into v_pk_{add,mul,fma}_f32.  Kernel-argument preloading is
+on (``-amdgpu-kernarg-preload-count=16``): a kernel's leading scalar and
+pointer arguments arrive in SGPRs with the wave, so the decode kernels'
+first loads need no scalar load of the kernarg segment (firmware without
+the feature runs the compiler's fallback loads instead).
 """
 import glob
 import os
@@ -26,6 +30,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     common = [hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
               "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+              "-mllvm", "-amdgpu-kernarg-preload-count=16",
               "-Wall", "-Wno-unused-function"]
     objs, procs = [], []
     for src in sources():

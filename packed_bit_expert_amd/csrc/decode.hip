@@ -144,12 +144,14 @@ __global__ __launch_bounds__(256) void k_resolve(const int32_t* ids, const uint8
 // pre-norm once (FP64) for its four waves.  A rejected slot reads a harmless
 // valid address and writes zeros, so the code after the loads is
 // straight-line and each chunk waits only for its own load.
+// The arguments its first loads depend on come first and one by one: the
+// library is built with kernarg preloading (-amdgpu-kernarg-preload-count),
+// so on gfx950 they arrive in SGPRs with the wave instead of through scalar
+// loads of the kernarg segment; the rest stay in DecodeArgs.
 template <int H, int I, int FMT, bool PRENORM, bool DUMP>
-__global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
-  // every argument the first loads depend on, fetched in one scalar batch
-  // (the compiler would otherwise fetch them in dependent rounds near use)
-  asm volatile("" ::"s"(a.x), "s"(a.pre), "s"(a.slots), "s"(a.hbuf), "s"(a.T), "s"(a.kmagic),
-               "s"(a.K), "s"(a.eps));
+__global__ __launch_bounds__(256) void k_dec_gateup(const SlotRef* pre, SlotRef* slots_ws,
+                                                    const uint16_t* x, uint64_t kmagic, int T,
+                                                    int K, int E, uint32_t flags, DecodeArgs a) {
   using S = GuShape<H>;
   using M = typename S::M;
   constexpr int LPR = M::LPR, CPL = M::CPL, RPS = M::RPS, NS = S::NS, RW = S::RW;
@@ -164,17 +166,17 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
   const int gw = blockIdx.x * 4 + wave;
   // all waves of a workgroup belong to one token (per_slot * K is a multiple of 4)
   const int nb = gw % per_slot, sj = gw / per_slot;
-  const bool live = sj < a.T * a.K;
-  const int sjc = live ? sj : a.T * a.K - 1;
-  const int t = (int)(((uint64_t)(uint32_t)sjc * a.kmagic) >> 32), j = sjc - t * a.K;
+  const bool live = sj < T * K;
+  const int sjc = live ? sj : T * K - 1;
+  const int t = (int)(((uint64_t)(uint32_t)sjc * kmagic) >> 32), j = sjc - t * K;
 
   // 0. the slot's expert (one 32-byte load of the pre-resolved table; without
   // one the load reads the workspace table, a harmless valid address, and
   // the slot is resolved below), then the activations, so that both are in
   // flight together
-  SlotRef sr = load_slot(a.pre ? a.pre + sjc : a.slots);
+  SlotRef sr = load_slot(pre ? pre + sjc : slots_ws);
   __builtin_amdgcn_sched_barrier(0);
-  const uint16_t* xt = a.x + (size_t)t * H;
+  const uint16_t* xt = x + (size_t)t * H;
   bf16x2 xp[CPL][16];
   constexpr int XPT = PRENORM ? (H / 8 + 255) / 256 : 1;  // 16-byte pieces of x per thread
   uint4 xraw[XPT];
@@ -186,14 +188,14 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  if (!a.pre) {
-    sr = resolve_slot(a.ids, a.wtab, a.stab, a.tsc, sjc, a.E, a.flags,
+  if (!pre) {
+    sr = resolve_slot(a.ids, a.wtab, a.stab, a.tsc, sjc, E, flags,
                       (nb == 0 && lane == 0 && live) ? a.err : nullptr);
-    if (nb == 0 && lane == 0 && live) a.slots[sj] = sr;
+    if (nb == 0 && lane == 0 && live) slots_ws[sj] = sr;
   }
   const bool ok = __builtin_amdgcn_readfirstlane(sr.ok) != 0;
-  const uint8_t* wbase = ok ? sr.w : (const uint8_t*)a.slots;
-  const uint8_t* sbase = ok ? sr.s : (const uint8_t*)a.slots;
+  const uint8_t* wbase = ok ? sr.w : (const uint8_t*)slots_ws;
+  const uint8_t* sbase = ok ? sr.s : (const uint8_t*)slots_ws;
   const size_t mat_nib = ok ? (size_t)I * (H / 2) : 0, mat_sc = ok ? (size_t)I * (H / G) : 0;
   const size_t row_nib = ok ? H / 2 : 0, row_sc = ok ? H / G : 0;
   const int li = lane % LPR, q = lane / LPR;
@@ -302,11 +304,11 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
 // then the slot-order BF16 combine (+ residual) of those rows.  The token's h
 // (all k slots, k * I BF16) is read once per workgroup into LDS; every lane
 // then takes its slices from there instead of re-reading them from L2.
+// Leading arguments as in k_dec_gateup (preloaded into SGPRs).
 template <int H, int I, int FMT, bool DUMP>
-__global__ __launch_bounds__(256) void k_dec_down(DecodeArgs a) {
-  // every argument the first loads depend on, fetched in one scalar batch
-  asm volatile("" ::"s"(a.pre), "s"(a.slots), "s"(a.hbuf), "s"(a.rw), "s"(a.residual),
-               "s"(a.out), "s"(a.T), "s"(a.K));
+__global__ __launch_bounds__(256) void k_dec_down(const SlotRef* pre, const SlotRef* slots_ws,
+                                                  const uint16_t* rw, const uint16_t* hbuf,
+                                                  const uint16_t* residual, int K, DecodeArgs a) {
   using D = DnShape<I>;
   using M = typename D::M;
   constexpr int LPR = M::LPR, CPL = M::CPL, RPS = M::RPS, NS = D::NS, ROWS = D::ROWS;
@@ -321,22 +323,22 @@ __global__ __launch_bounds__(256) void k_dec_down(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // a scalar: the slot indices
   const int li = lane % LPR, q = lane / LPR;
-  const SlotRef* slots = a.pre ? a.pre : a.slots;
+  const SlotRef* slots = pre ? pre : slots_ws;
 
   // 1. loads, in this order: the wave's first slot (its weights depend on
   // it), the combine's operands, the token's h, then the slot's scales and
   // weights.  Everything is unconditional with clamped indices, so the loads
   // go out back to back and each value is waited for only where it is used.
   // A wave without a slot (k < 4) works on the last one and discards it.
-  const int j0 = min(wave, a.K - 1);
-  const SlotRef sr0 = load_slot(slots + t * a.K + j0);
+  const int j0 = min(wave, K - 1);
+  const SlotRef sr0 = load_slot(slots + t * K + j0);
   uint16_t rwv[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) rwv[j] = a.rw[t * a.K + min(j, a.K - 1)];
+  for (int j = 0; j < 8; ++j) rwv[j] = rw[t * K + min(j, K - 1)];
   // (without a residual the load reads a harmless valid address, unused)
-  const uint16_t resv = *(a.residual ? a.residual + (size_t)t * H + m0 + tid % ROWS : a.rw);
-  const int npc = a.K * I / 8;
-  const uint16_t* ht = a.hbuf + (size_t)t * a.K * I;
+  const uint16_t resv = *(residual ? residual + (size_t)t * H + m0 + tid % ROWS : rw);
+  const int npc = K * I / 8;
+  const uint16_t* ht = hbuf + (size_t)t * K * I;
   uint4 hv[HPT];
 #pragma unroll
   for (int u = 0; u < HPT; ++u) hv[u] = ldg16(ht + 8 * min(tid + 256 * u, npc - 1));
@@ -380,7 +382,7 @@ __global__ __launch_bounds__(256) void k_dec_down(DecodeArgs a) {
       const uint16_t y = ok ? f64_to_bf16(tot * (double)sr.td) : (uint16_t)0;
       ys[j][r] = y;
       if constexpr (DUMP) {
-        if (a.dy) a.dy[((size_t)t * a.K + j) * H + m0 + r] = y;
+        if (a.dy) a.dy[((size_t)t * K + j) * H + m0 + r] = y;
       }
     }
   };
@@ -395,10 +397,10 @@ __global__ __launch_bounds__(256) void k_dec_down(DecodeArgs a) {
   for (int u = 0; u < HPT; ++u)
     if (tid + 256 * u < npc) *(uint4*)(hs + 8 * (tid + 256 * u)) = hv[u];
   lds_barrier();
-  if (wave < a.K) finish(wave, sr0, wv, sv);
+  if (wave < K) finish(wave, sr0, wv, sv);
   // 3. slots 4..k-1 (k > 4), one more per wave
-  for (int j = wave + 4; j < a.K; j += 4) {
-    const SlotRef sr = load_slot(slots + t * a.K + j);
+  for (int j = wave + 4; j < K; j += 4) {
+    const SlotRef sr = load_slot(slots + t * K + j);
     issue(sr, wv, sv);
     finish(j, sr, wv, sv);
   }
@@ -408,8 +410,8 @@ __global__ __launch_bounds__(256) void k_dec_down(DecodeArgs a) {
     uint16_t acc = 0;  // +0
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (j < a.K) acc = combine_step(acc, rwv[j], ys[j][tid]);
-    if (a.residual) acc = residual_add(resv, acc);
+      if (j < K) acc = combine_step(acc, rwv[j], ys[j][tid]);
+    if (residual) acc = residual_add(resv, acc);
     a.out[(size_t)t * H + m] = acc;
   }
 }
@@ -427,10 +429,12 @@ hipError_t launch_variant(const DecodeArgs& a0, hipStream_t s) {
   a.kmagic = (uint64_t)((1ull << 32) / (uint64_t)a.K) + 1;
   const int waves = a.T * a.K * ((I + GuShape<H>::RW - 1) / GuShape<H>::RW);
   const hipError_t e = launch_kernel(MOE_KERNEL_DECODE_GATE_UP, k_dec_gateup<H, I, FMT, PRENORM, DUMP>,
-                                     dim3((waves + 3) / 4), dim3(256), 0, s, a);
+                                     dim3((waves + 3) / 4), dim3(256), 0, s, a.pre, a.slots, a.x,
+                                     a.kmagic, a.T, a.K, a.E, a.flags, a);
   if (e != hipSuccess) return e;
   return launch_kernel(MOE_KERNEL_DECODE_DOWN, k_dec_down<H, I, FMT, DUMP>,
-                       dim3(a.T * (H / DnShape<I>::ROWS)), dim3(256), 0, s, a);
+                       dim3(a.T * (H / DnShape<I>::ROWS)), dim3(256), 0, s, a.pre,
+                       (const SlotRef*)a.slots, a.rw, (const uint16_t*)a.hbuf, a.residual, a.K, a);
 }
 
 template <int H, int I, int FMT>
