@@ -565,22 +565,21 @@ __device__ __forceinline__ int expert_of(const int* pre, int E, int it) {
   return lo;
 }
 
+// The arguments of the prologue's first loads come first and one by one
+// (preloaded into SGPRs, as for the decode kernels); the rest are in
+// BatchedArgs.
 template <int FMT, int MODE, int KS, bool A4>
-__global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedArgs a) {
-  // the arguments of the prologue's loads, fetched in one scalar batch (the
-  // compiler would otherwise fetch them in dependent rounds near use)
-  asm volatile("" ::"s"(a.ids), "s"(a.wtab), "s"(a.stab), "s"(a.tsc), "s"(a.x), "s"(a.hbuf),
-               "s"(a.ybuf), "s"(a.hq), "s"(a.du), "s"(a.dg), "s"(a.dv), "s"(a.dh), "s"(a.dy),
-               "s"(a.err), "s"(a.T), "s"(a.K), "s"(a.E), "s"(a.I), "s"(a.H), "s"(a.ncu),
-               "s"(a.flags));
+__global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(
+    const int32_t* ids, const uint8_t* const* wtab, const uint8_t* const* stab, const float* tsc,
+    int T, int K, int E, int H, int I, int ncu_dev, int wg_per_cu, uint32_t flags, BatchedArgs a) {
   static_assert(!A4 || FMT == MOE_SCALE_E8M0_G32, "W4A4 pairs E8M0 scales on both operands");
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   constexpr int NMAT = MODE == 0 ? 2 : 1;
   constexpr int G = FMT == MOE_SCALE_E4M3_G16 ? 16 : 32;
   // vector loads of one stage, per lane
   constexpr int NLOADS = (2 * KS + (KS + 1) / 2) * NMAT;
-  const int Kd = MODE == 0 ? a.H : a.I;
-  const int Nd = MODE == 0 ? a.I : a.H;
+  const int Kd = MODE == 0 ? H : I;
+  const int Nd = MODE == 0 ? I : H;
   const int ntiles = Nd / kBN, nst = Kd / (kKS * KS);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ln = lane & 15, gl = lane >> 4;
@@ -588,56 +587,59 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
   uint16_t* xs = lds;                   // [kMC][ldx]
   int* list = (int*)(lds + kMC * ldx);  // [kMC]
   int* cnt = list + kMC;                // [E]
-  int* pre = cnt + a.E;                 // [E + 1]: passes of the experts before e
-  int* wcnt = pre + a.E + 1;            // [kBW]
+  int* pre = cnt + E;                 // [E + 1]: passes of the experts before e
+  int* wcnt = pre + E + 1;            // [kBW]
   __shared__ int cut[2];                // E4M3: this CU's first tile and the next CU's
   // the expert tables, staged once: weight bases, scale bases, tensor scales
-  const int tab_off = (kMC * ldx * 2 + (kMC + 2 * a.E + 1 + kBW) * 4 + 7) & ~7;  // bytes
+  const int tab_off = (kMC * ldx * 2 + (kMC + 2 * E + 1 + kBW) * 4 + 7) & ~7;  // bytes
   const uint8_t** tw = (const uint8_t**)((char*)lds + tab_off);
-  const uint8_t** ts = tw + a.E;
-  float* tt = (float*)(ts + a.E);
+  const uint8_t** ts = tw + E;
+  float* tt = (float*)(ts + E);
   // gate/up under W4A4: one tile's h, [16 tokens][64 rows] BF16; E4M3: a
   // 256-byte zero block (the A operand of the lanes whose group an MFMA skips)
-  uint16_t* hl = (uint16_t*)((char*)lds + ((tab_off + a.E * (2 * (int)sizeof(void*) + 4) + 15) & ~15));
-  const int npairs = a.T * a.K;
+  uint16_t* hl = (uint16_t*)((char*)lds + ((tab_off + E * (2 * (int)sizeof(void*) + 4) + 15) & ~15));
+  const int npairs = T * K;
   // this workgroup's CU and its rank among the CU's workgroups (scalars:
   // computed once, ahead of any wave-dependent branch)
-  const int ncu = a.ncu, P = (int)gridDim.x / ncu;
+  const int ncu = ncu_dev, P = wg_per_cu;  // the grid is P * ncu workgroups
   const int cu = (int)blockIdx.x % ncu, rank = (int)blockIdx.x / ncu;
 
   // 1. the items: per-expert pair counts, then the prefix of their passes.
   // The first 256 ids are requested with the expert tables, so that both
   // round trips overlap.
-  const int id0 = tid < npairs ? a.ids[tid] : -1;
+  const int id0 = tid < npairs ? ids[tid] : -1;
   if (FMT == MOE_SCALE_E4M3_G16 && tid < 64) ((uint32_t*)hl)[tid] = 0u;
-  for (int e = tid; e < a.E; e += 64 * kBW) {
+  // the other arguments, fetched in one scalar batch behind the first loads
+  // (the compiler would otherwise fetch them in dependent rounds near use)
+  asm volatile("" ::"s"(a.x), "s"(a.hbuf), "s"(a.ybuf), "s"(a.hq), "s"(a.err));
+  for (int e = tid; e < E; e += 64 * kBW) {
     cnt[e] = 0;
-    tw[e] = a.wtab[e];
-    ts[e] = a.stab[e];
-    tt[e] = FMT == MOE_SCALE_E4M3_G16 ? a.tsc[2 * e + MODE] : 1.f;
+    tw[e] = wtab[e];
+    ts[e] = stab[e];
+    tt[e] = FMT == MOE_SCALE_E4M3_G16 ? tsc[2 * e + MODE] : 1.f;
   }
   __syncthreads();
   bool bad = false;
   for (int p = tid; p < npairs; p += 64 * kBW) {
-    const int e = p == tid ? id0 : a.ids[p];
-    if ((unsigned)e < (unsigned)a.E) atomicAdd(&cnt[e], 1);
+    const int e = p == tid ? id0 : ids[p];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
     else bad = true;
   }
-  if (MODE == 0 && blockIdx.x == 0 && bad && (a.flags & MOE_FLAG_CHECK_IDS)) atomicOr(a.err, kErrBadId);
+  if (MODE == 0 && blockIdx.x == 0 && bad && (flags & MOE_FLAG_CHECK_IDS)) atomicOr(a.err, kErrBadId);
   __syncthreads();
   auto aligned = [&](int e) {
-    return !(a.flags & MOE_FLAG_CHECK_IDS) || ((((uintptr_t)tw[e]) | ((uintptr_t)ts[e])) & 15u) == 0;
+    return !(flags & MOE_FLAG_CHECK_IDS) || ((((uintptr_t)tw[e]) | ((uintptr_t)ts[e])) & 15u) == 0;
   };
   // a selected expert with a misaligned base is reported once and skipped
   if (blockIdx.x == 0)
-    for (int e = tid; e < a.E; e += 64 * kBW)
+    for (int e = tid; e < E; e += 64 * kBW)
       if (cnt[e] > 0 && !aligned(e)) atomicOr(a.err, kErrAlign);
   if (wave == 0) {
-    const int per = (a.E + 63) / 64;
+    const int per = (E + 63) / 64;
     int mine = 0;
     for (int i = 0; i < per; ++i) {
       const int e = lane * per + i;
-      if (e < a.E) mine += (cnt[e] + kMC - 1) / kMC;
+      if (e < E) mine += (cnt[e] + kMC - 1) / kMC;
     }
     int incl = mine;
 #pragma unroll
@@ -648,12 +650,12 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
     int run = incl - mine;
     for (int i = 0; i < per; ++i) {
       const int e = lane * per + i;
-      if (e < a.E) {
+      if (e < E) {
         pre[e] = run;
         run += (cnt[e] + kMC - 1) / kMC;
       }
     }
-    if (lane == 63) pre[a.E] = incl;
+    if (lane == 63) pre[E] = incl;
     if constexpr (FMT == MOE_SCALE_E4M3_G16) {
       // E4M3: a tile of a pass of more than kMC / 2 tokens runs twice the
       // MFMAs and about 1.75 times the VALU work of a smaller pass's tile
@@ -667,7 +669,7 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
       int cmine = 0;
       for (int i = 0; i < per; ++i) {
         const int e = lane * per + i;
-        if (e < a.E) cmine += kLight * ((cnt[e] + kMC - 1) / kMC) + (kHeavy - kLight) * heavy_passes(cnt[e]);
+        if (e < E) cmine += kLight * ((cnt[e] + kMC - 1) / kMC) + (kHeavy - kLight) * heavy_passes(cnt[e]);
       }
       long long cincl = cmine;
 #pragma unroll
@@ -680,14 +682,14 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
       for (int k = 0; k < 2; ++k) {
         const long long B = W * (cu + k) / ncu;
         if (B >= W) {
-          if (lane == 0) cut[k] = pre[a.E] * ntiles;
+          if (lane == 0) cut[k] = pre[E] * ntiles;
           continue;
         }
         long long C = (cincl - cmine) * ntiles;
         if (B < C || B >= cincl * ntiles) continue;
         for (int i = 0; i < per; ++i) {
           const int e = lane * per + i;
-          if (e >= a.E) break;
+          if (e >= E) break;
           const int hn = heavy_passes(cnt[e]) * ntiles;
           const long long ce = (long long)kLight * ((cnt[e] + kMC - 1) / kMC) * ntiles + (long long)(kHeavy - kLight) * hn;
           if (B < C + ce) {
@@ -711,7 +713,7 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
   // larger shares.  Splitting the tiles evenly over blockIdx instead gave
   // the two workgroups of a CU equal counts, so CUs carried 2 or 4 tiles
   // at c2 where 3 or 4 suffice.
-  const long long ntot = (long long)pre[a.E] * ntiles;
+  const long long ntot = (long long)pre[E] * ntiles;
   if (rank >= P) return;
   // (the cut points come from LDS: read them as wave-uniform scalars, or the
   // loop's tile and stage arithmetic would all run on the VALU)
@@ -736,13 +738,13 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
   // a new item: its expert, pass and pairs, then its token rows (direct
   // loads, waited for later)
   auto setup_item = [&](int item) {
-    const int e = expert_of(pre, a.E, item);
+    const int e = expert_of(pre, E, item);
     it.e = e;
     it.p = item - pre[e];
     it.mcnt = min(kMC, cnt[e] - kMC * it.p);
     it.tscale = (double)tt[e];
     it.ok = aligned(e);
-    collect_pairs(a.ids, id0, npairs, e, kMC * it.p, list, wcnt);
+    collect_pairs(ids, id0, npairs, e, kMC * it.p, list, wcnt);
     stage_rows<MODE, A4>(a, list, it.mcnt, Kd, ldx, xs, wave, lane);
   };
   // row pointers of this lane for tile column block j of the current item
@@ -751,19 +753,19 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
     const size_t nn = iok ? (size_t)n : 0;
     if (MODE == 0) {
       wrow[0] = iw + nn * rowb;
-      wrow[1] = wrow[0] + (iok ? (size_t)a.I * rowb : 0);
+      wrow[1] = wrow[0] + (iok ? (size_t)I * rowb : 0);
       srow[0] = isc + nn * rows;
-      srow[1] = srow[0] + (iok ? (size_t)a.I * rows : 0);
+      srow[1] = srow[0] + (iok ? (size_t)I * rows : 0);
     } else {
-      wrow[0] = wrow[1] = iw + (iok ? (size_t)a.I * a.H + nn * rowb : 0);
-      srow[0] = srow[1] = isc + (iok ? 2 * (size_t)a.I * (a.H / G) + nn * rows : 0);
+      wrow[0] = wrow[1] = iw + (iok ? (size_t)I * H + nn * rowb : 0);
+      srow[0] = srow[1] = isc + (iok ? 2 * (size_t)I * (H / G) + nn * rows : 0);
     }
   };
   auto issue = [&](WStep<FMT, NMAT>(&W)[KS], StageScales<FMT, NMAT, KS>& SQ, int g) {
     const int tile = g / nst, st = g - tile * nst;
     if (tile / ntiles != iss_item) {
       iss_item = tile / ntiles;
-      const int e = expert_of(pre, a.E, iss_item);
+      const int e = expert_of(pre, E, iss_item);
       iok = aligned(e);
       // a rejected expert reads a harmless buffer: every step its first 36 bytes
       iw = iok ? tw[e] : (const uint8_t*)a.x;
@@ -781,7 +783,7 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
     if (MODE == 0 && a.du && first_tile % ntiles == 0) {
       for (int r = wave; r < it.mcnt; r += kBW) {
         const uint16_t* row = xs + r * ldx;
-        const int t = list[r] / a.K;
+        const int t = list[r] / K;
         for (int k = lane; k < Kd; k += 64) a.du[(size_t)t * Kd + k] = row[k];
       }
     }
@@ -862,7 +864,7 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
           const uint16_t gb = f64_to_bf16(acc[0][i] * it.tscale);
           const uint16_t ub = f64_to_bf16(acc[1][i] * it.tscale);
           const uint16_t h = silu_mul_bf16(gb, ub);
-          const size_t o = (size_t)pair * a.I + n;
+          const size_t o = (size_t)pair * I + n;
           if constexpr (A4) hl[m * 64 + wave * 16 + ln] = h;
           else a.hbuf[o] = h;
           if (a.dg) a.dg[o] = gb;
@@ -870,7 +872,7 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
           if (a.dh) a.dh[o] = h;
         } else {
           const uint16_t y = f64_to_bf16(acc[0][i] * it.tscale);
-          const size_t o = (size_t)pair * a.H + n;
+          const size_t o = (size_t)pair * H + n;
           a.ybuf[o] = y;
           if (a.dy) a.dy[o] = y;
         }
@@ -889,9 +891,9 @@ __global__ __launch_bounds__(64 * kBW, kWgPerCu[MODE]) void k_bat_gemm(BatchedAr
         uint32_t sc;
         const uint4 codes = mxfp4_block(w, sc);
         const int n0 = (tile % ntiles) * kBN + 32 * half;  // the block's first row
-        uint8_t* row = a.hq + (size_t)list[m] * mxfp4_row_bytes(a.I);
+        uint8_t* row = a.hq + (size_t)list[m] * mxfp4_row_bytes(I);
         *(uint4*)(row + n0 / 2) = codes;
-        row[a.I / 2 + n0 / 32] = (uint8_t)sc;
+        row[I / 2 + n0 / 32] = (uint8_t)sc;
       }
     }
 #pragma unroll
@@ -1120,7 +1122,8 @@ hipError_t launch_gemm_ks(const BatchedArgs& a, hipStream_t s) {
   BatchedArgs b = a;
   b.ncu = cu_count();
   return launch_kernel(MODE == 0 ? MOE_KERNEL_BATCHED_GATE_UP : MOE_KERNEL_BATCHED_DOWN,
-                       k_bat_gemm<FMT, MODE, KS, A4>, dim3(per * b.ncu), dim3(64 * kBW), lds, s, b);
+                       k_bat_gemm<FMT, MODE, KS, A4>, dim3(per * b.ncu), dim3(64 * kBW), lds, s,
+                       b.ids, b.wtab, b.stab, b.tsc, b.T, b.K, b.E, b.H, b.I, b.ncu, per, b.flags, b);
 }
 
 // K steps per pipeline stage: the largest divisor of the step count up to 2
