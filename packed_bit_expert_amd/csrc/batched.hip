@@ -971,29 +971,6 @@ __device__ __forceinline__ double row_rscale(double ss, int H, float eps, double
   return 1.0 / sqrt((red[0] + red[1] + red[2] + red[3]) / (double)H + (double)eps);
 }
 
-__device__ __forceinline__ double sq8(uint4 v) {
-  const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-  double ss = 0.0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const double lo = __uint_as_float(w4[q] << 16), hi = __uint_as_float(w4[q] & 0xFFFF0000u);
-    ss += lo * lo + hi * hi;
-  }
-  return ss;
-}
-
-__device__ __forceinline__ uint4 scale8(uint4 v, double rs) {
-  const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-  uint32_t o4[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t lo = f64_to_bf16((double)__uint_as_float(w4[q] << 16) * rs);
-    const uint32_t hi = f64_to_bf16((double)__uint_as_float(w4[q] & 0xFFFF0000u) * rs);
-    o4[q] = lo | (hi << 16);
-  }
-  return make_uint4(o4[0], o4[1], o4[2], o4[3]);
-}
-
 template <bool NORM, bool Q>
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
                                                  const uint16_t* __restrict__ rw,
@@ -1035,8 +1012,8 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
     *(uint4*)(out + (size_t)t * H + 8 * m8) = o;
   }
   if constexpr (NORM) {
-    const double rs = row_rscale(live ? sq8(o) : 0.0, H, eps, red);
-    const uint4 uv = scale8(o, rs);
+    const double rs = row_rscale(live ? sumsq8_bf16(o) : 0.0, H, eps, red);
+    const uint4 uv = scale8_bf16(o, rs);
     if (live) *(uint4*)(u + (size_t)t * H + 8 * m8) = uv;
     if constexpr (Q) mxfp4_store8(uv, m8, uq + (size_t)t * mxfp4_row_bytes(H), H, live);
   }
@@ -1057,13 +1034,13 @@ __global__ __launch_bounds__(256) void k_prenorm(const uint16_t* __restrict__ x,
   for (int i = 0; i < 2; ++i) {
     const int k8 = threadIdx.x + 256 * i;
     v[i] = k8 < H / 8 ? ldg16(x + (size_t)t * H + 8 * k8) : make_uint4(0u, 0u, 0u, 0u);
-    ss += sq8(v[i]);
+    ss += sumsq8_bf16(v[i]);
   }
   const double rs = row_rscale(ss, H, eps, red);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int k8 = threadIdx.x + 256 * i;
-    const uint4 uv = scale8(v[i], rs);
+    const uint4 uv = scale8_bf16(v[i], rs);
     if (k8 < H / 8) *(uint4*)(u + (size_t)t * H + 8 * k8) = uv;
     if constexpr (Q) mxfp4_store8(uv, k8, uq + (size_t)t * mxfp4_row_bytes(H), H, k8 < H / 8);
   }

@@ -99,26 +99,32 @@ __device__ __forceinline__ void unpack16_lds(const uint16_t* p, bf16x2 (&xp)[16]
 __device__ __forceinline__ SlotRef resolve_slot(const int32_t* ids, const uint8_t* const* wtab,
                                                 const uint8_t* const* stab, const float* tsc,
                                                 int i, int E, uint32_t flags, int* err) {
+  // Every table read comes before the error atomics (at a clamped index), so
+  // the compiler knows nothing in this kernel has written those words yet and
+  // reads them with scalar loads when the slot index is uniform: a vector
+  // load here would leave a register pending where the path without this
+  // call joins, and the compiler then waits for every load in flight (the
+  // activations included) before the weight loads can go out.
   SlotRef r;
   r.pad = 0;
-  r.tg = r.td = 1.f;
   const int e = ids[i];
+  const int ec = min(max(e, 0), E - 1);
+  r.w = wtab[ec];
+  r.s = stab[ec];
+  r.tg = tsc ? tsc[2 * ec] : 1.f;
+  r.td = tsc ? tsc[2 * ec + 1] : 1.f;
+  r.ok = 1;
   if ((flags & MOE_FLAG_CHECK_IDS) && (e < 0 || e >= E)) {
     if (err) atomicOr(err, kErrBadId);
     r.w = r.s = nullptr;
+    r.tg = r.td = 1.f;
     r.ok = 0;
     return r;
   }
-  r.w = wtab[e];
-  r.s = stab[e];
-  r.ok = 1;
   if ((flags & MOE_FLAG_CHECK_IDS) && ((((uintptr_t)r.w) | ((uintptr_t)r.s)) & 15u)) {
     if (err) atomicOr(err, kErrAlign);
+    r.tg = r.td = 1.f;
     r.ok = 0;
-  }
-  if (tsc && r.ok) {
-    r.tg = tsc[2 * e];
-    r.td = tsc[2 * e + 1];
   }
   return r;
 }
@@ -233,13 +239,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const SlotRef* pre, SlotRef*
     for (int u = 0; u < XPT; ++u) {
       const int k8 = threadIdx.x + 256 * u;
       if (k8 >= H / 8) break;
-      const uint4 v = xraw[u];
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const double lo = __uint_as_float(w4[k] << 16), hi = __uint_as_float(w4[k] & 0xFFFF0000u);
-        ss += lo * lo + hi * hi;
-      }
+      ss += sumsq8_bf16(xraw[u]);
     }
     ss = seg_finish<32, double>(ss, lane);
     if (lane == 0) red[wave] = ss;
@@ -250,15 +250,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const SlotRef* pre, SlotRef*
     for (int u = 0; u < XPT; ++u) {
       const int k8 = threadIdx.x + 256 * u;
       if (k8 >= H / 8) break;
-      const uint32_t w4[4] = {xraw[u].x, xraw[u].y, xraw[u].z, xraw[u].w};
-      uint32_t o4[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t lo = f64_to_bf16((double)__uint_as_float(w4[k] << 16) * rs);
-        const uint32_t hi = f64_to_bf16((double)__uint_as_float(w4[k] & 0xFFFF0000u) * rs);
-        o4[k] = lo | (hi << 16);
-      }
-      *(uint4*)(xs + 8 * k8) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+      *(uint4*)(xs + 8 * k8) = scale8_bf16(xraw[u], rs);
     }
     __syncthreads();
 #pragma unroll
