@@ -167,6 +167,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const SlotRef* pre, SlotRef*
   // The wave's slot and token, in scalar registers and without a division
   // by a run-time value: these indices stand in front of the first load.
   constexpr int per_slot = (I + RW - 1) / RW;
+  static_assert(per_slot % 4 == 0, "the waves of a workgroup share one slot");
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int gw = blockIdx.x * 4 + wave;
@@ -274,21 +275,30 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const SlotRef* pre, SlotRef*
     for (int i = 0; i < CPL; ++i) p[st] += chunk_dot<FMT>(wv[st][i], sv[st][i], xp[i]);
   }
   const double tot = seg_reduce<NS, LPR>(p, lane);
-  const double oth = xor_lane<LPR>(tot, lane);  // the same n of the other matrix
-  const int v = li / (LPR / NS);             // load set whose sum this lane holds
-  const int n = n0 + v * (RPS / 2) + (q >> 1);
-  if ((li % (LPR / NS)) == 0 && (q & 1) == 0 && n < I) {
-    const double tg = (double)sr.tg;
-    uint16_t gb = f64_to_bf16(tot * tg), ub = f64_to_bf16(oth * tg);
-    uint16_t h = silu_mul_bf16(gb, ub);
-    if (!ok) gb = ub = h = 0;
-    const size_t o = (size_t)sj * I + n;
-    a.hbuf[o] = h;
-    if constexpr (DUMP) {
-      if (a.dg) a.dg[o] = gb;
-      if (a.dv) a.dv[o] = ub;
-      if (a.dh) a.dh[o] = h;
-    }
+
+  // 4. the workgroup's row sums meet in LDS and wave 0 finishes its 4 * RW
+  // rows, one lane each: BF16 g and v, SiLU(g) * v, the h store.  Per wave
+  // the epilogue would run with only RW lanes active; once per workgroup its
+  // instructions are issued a quarter as often.  The four waves share the
+  // slot (per_slot is a multiple of 4) and hold consecutive row blocks.
+  __shared__ double rsum[4][NS][RPS];  // [wave][load set][q = matrix + 2 * row]
+  if ((li % (LPR / NS)) == 0) rsum[wave][li / (LPR / NS)][q] = tot;
+  lds_barrier();
+  if (wave != 0 || lane >= 4 * RW) return;
+  const int w = lane / RW, r = lane % RW;
+  const int v = r / (RPS / 2), qh = r % (RPS / 2);
+  const int n = (nb + w) * RW + r;
+  if (n >= I) return;
+  const double tg = (double)sr.tg;
+  uint16_t gb = f64_to_bf16(rsum[w][v][2 * qh] * tg), ub = f64_to_bf16(rsum[w][v][2 * qh + 1] * tg);
+  uint16_t h = silu_mul_bf16(gb, ub);
+  if (!ok) gb = ub = h = 0;
+  const size_t o = (size_t)sj * I + n;
+  a.hbuf[o] = h;
+  if constexpr (DUMP) {
+    if (a.dg) a.dg[o] = gb;
+    if (a.dv) a.dv[o] = ub;
+    if (a.dh) a.dh[o] = h;
   }
 }
 
