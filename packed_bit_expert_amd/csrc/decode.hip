@@ -306,8 +306,9 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const SlotRef* pre, SlotRef*
 // then the slot-order BF16 combine (+ residual) of those rows.  The token's h
 // (all k slots, k * I BF16) is read once per workgroup into LDS; every lane
 // then takes its slices from there instead of re-reading them from L2.
-// Leading arguments as in k_dec_gateup (preloaded into SGPRs).
-template <int H, int I, int FMT, bool DUMP>
+// Leading arguments as in k_dec_gateup (preloaded into SGPRs).  KMAX (4 or
+// 8) bounds k, so that at top-4 no load or LDS slot is spent on slots 5..8.
+template <int H, int I, int FMT, bool DUMP, int KMAX>
 __global__ __launch_bounds__(256) void k_dec_down(const SlotRef* pre, const SlotRef* slots_ws,
                                                   const uint16_t* rw, const uint16_t* hbuf,
                                                   const uint16_t* residual, int K, DecodeArgs a) {
@@ -315,9 +316,9 @@ __global__ __launch_bounds__(256) void k_dec_down(const SlotRef* pre, const Slot
   using M = typename D::M;
   constexpr int LPR = M::LPR, CPL = M::CPL, RPS = M::RPS, NS = D::NS, ROWS = D::ROWS;
   constexpr int G = group_of<FMT>();
-  constexpr int HPT = (I + 255) / 256;  // 16-byte pieces of h per thread for k <= 8
-  __shared__ uint16_t ys[8][ROWS];
-  __shared__ __attribute__((aligned(16))) uint16_t hs[8 * I];
+  constexpr int HPT = (KMAX * I / 8 + 255) / 256;  // 16-byte pieces of h per thread
+  __shared__ uint16_t ys[KMAX][ROWS];
+  __shared__ __attribute__((aligned(16))) uint16_t hs[KMAX * I];
 
   const int nblk = H / ROWS;
   const int mb = blockIdx.x % nblk, t = blockIdx.x / nblk;
@@ -334,9 +335,9 @@ __global__ __launch_bounds__(256) void k_dec_down(const SlotRef* pre, const Slot
   // A wave without a slot (k < 4) works on the last one and discards it.
   const int j0 = min(wave, K - 1);
   const SlotRef sr0 = load_slot(slots + t * K + j0);
-  uint16_t rwv[8];
+  uint16_t rwv[KMAX];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) rwv[j] = rw[t * K + min(j, K - 1)];
+  for (int j = 0; j < KMAX; ++j) rwv[j] = rw[t * K + min(j, K - 1)];
   // (without a residual the load reads a harmless valid address, unused)
   const uint16_t resv = *(residual ? residual + (size_t)t * H + m0 + tid % ROWS : rw);
   const int npc = K * I / 8;
@@ -401,17 +402,19 @@ __global__ __launch_bounds__(256) void k_dec_down(const SlotRef* pre, const Slot
   lds_barrier();
   if (wave < K) finish(wave, sr0, wv, sv);
   // 3. slots 4..k-1 (k > 4), one more per wave
-  for (int j = wave + 4; j < K; j += 4) {
-    const SlotRef sr = load_slot(slots + t * K + j);
-    issue(sr, wv, sv);
-    finish(j, sr, wv, sv);
+  if constexpr (KMAX > 4) {
+    for (int j = wave + 4; j < K; j += 4) {
+      const SlotRef sr = load_slot(slots + t * K + j);
+      issue(sr, wv, sv);
+      finish(j, sr, wv, sv);
+    }
   }
   __syncthreads();
   if (tid < ROWS) {
     const int m = m0 + tid;
     uint16_t acc = 0;  // +0
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < KMAX; ++j)
       if (j < K) acc = combine_step(acc, rwv[j], ys[j][tid]);
     if (residual) acc = residual_add(resv, acc);
     a.out[(size_t)t * H + m] = acc;
@@ -434,7 +437,11 @@ hipError_t launch_variant(const DecodeArgs& a0, hipStream_t s) {
                                      dim3((waves + 3) / 4), dim3(256), 0, s, a.pre, a.slots, a.x,
                                      a.kmagic, a.T, a.K, a.E, a.flags, a);
   if (e != hipSuccess) return e;
-  return launch_kernel(MOE_KERNEL_DECODE_DOWN, k_dec_down<H, I, FMT, DUMP>,
+  if (a.K <= 4)
+    return launch_kernel(MOE_KERNEL_DECODE_DOWN, k_dec_down<H, I, FMT, DUMP, 4>,
+                         dim3(a.T * (H / DnShape<I>::ROWS)), dim3(256), 0, s, a.pre,
+                         (const SlotRef*)a.slots, a.rw, (const uint16_t*)a.hbuf, a.residual, a.K, a);
+  return launch_kernel(MOE_KERNEL_DECODE_DOWN, k_dec_down<H, I, FMT, DUMP, 8>,
                        dim3(a.T * (H / DnShape<I>::ROWS)), dim3(256), 0, s, a.pre,
                        (const SlotRef*)a.slots, a.rw, (const uint16_t*)a.hbuf, a.residual, a.K, a);
 }

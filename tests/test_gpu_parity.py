@@ -263,6 +263,26 @@ def test_ragged_and_small_shapes(shape, T, flags):
     GH.compare(out, ref, "out")
 
 
+@pytest.mark.parametrize("K,T,flags", [(1, 1, 0), (2, 1, 0), (3, 1, M.FLAG_PRENORM), (5, 1, 0),
+                                       (6, 3, M.FLAG_FORCE_DECODE), (7, 1, M.FLAG_PRENORM),
+                                       (8, 2, M.FLAG_FORCE_DECODE | M.FLAG_PRENORM)])
+def test_decode_top_k_other_than_four(K, T, flags):
+    """The decode kernels at top-k below and above four: below, waves without
+    a slot of their own work on the last one and discard it; above, the down
+    kernel's waves take a second slot each (its top-8 build)."""
+    banner(f"decode top_k={K} H={MID.hidden} T={T} flags={flags}")
+    L = GH.Layer(MID, S.FMT_E8M0_G32, 6)
+    x = S.activations(9, 0, T, T, MID.hidden)
+    ids, rw = S.routing_uniform(9, 0, T, T, MID.experts, K)
+    r = S.activations(10, 0, T, T, MID.hidden)
+    out, d, st = L.gpu(x, ids, rw, residual=r, flags=flags, dumps=True)
+    assert st == 0
+    ref, rd = L.oracle(x, ids, rw, residual=r, prenorm=bool(flags & M.FLAG_PRENORM), dumps=True)
+    for k in ("h", "y"):
+        GH.compare(d[k], rd[k], f"k={K} {k}")
+    GH.compare(out, ref, f"k={K} out")
+
+
 def test_prenorm_residual_decode(layer_mx):
     banner("pre-norm + residual, T=1 decode and T=3 batched")
     for T in (1, 3):
