@@ -82,6 +82,14 @@ __device__ __forceinline__ void unpack16(const uint16_t* p, bf16x2 (&xp)[16]) {
   }
 }
 
+// LDS staging of activations in 80-byte segments: each 32-value (64-byte)
+// segment of x or h is followed by 16 bytes of padding.  Every lane reads
+// one segment piece by piece, 16 lanes of a row reading 16 consecutive
+// segments with one instruction; at a 64-byte stride those 16 addresses
+// fall into two 16-byte bank slots of every 128 bytes (an 8-way conflict),
+// at 80 bytes they take 8 distinct slots of 128 bytes and 16 of 256.
+constexpr int kSeg = 40;  // BF16 values per staged segment (32 + 8 padding)
+
 __device__ __forceinline__ void unpack16_lds(const uint16_t* p, bf16x2 (&xp)[16]) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -162,7 +170,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const SlotRef* pre, SlotRef*
   using M = typename S::M;
   constexpr int LPR = M::LPR, CPL = M::CPL, RPS = M::RPS, NS = S::NS, RW = S::RW;
   constexpr int G = group_of<FMT>();
-  __shared__ __attribute__((aligned(16))) uint16_t xs[PRENORM ? H : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[PRENORM ? (H / 32) * kSeg : 8];
   __shared__ double red[4];
   // The wave's slot and token, in scalar registers and without a division
   // by a run-time value: these indices stand in front of the first load.
@@ -251,14 +259,15 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const SlotRef* pre, SlotRef*
     for (int u = 0; u < XPT; ++u) {
       const int k8 = threadIdx.x + 256 * u;
       if (k8 >= H / 8) break;
-      *(uint4*)(xs + 8 * k8) = scale8_bf16(xraw[u], rs);
+      *(uint4*)(xs + kSeg * (k8 >> 2) + 8 * (k8 & 3)) = scale8_bf16(xraw[u], rs);
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) unpack16_lds(xs + 32 * (li + LPR * i), xp[i]);
+    for (int i = 0; i < CPL; ++i) unpack16_lds(xs + kSeg * (li + LPR * i), xp[i]);
     if constexpr (DUMP) {
       if (a.du && nb < 4 && j == 0 && live)
-        for (int k = threadIdx.x; k < H; k += 256) a.du[(size_t)t * H + k] = xs[k];
+        for (int k = threadIdx.x; k < H; k += 256)
+          a.du[(size_t)t * H + k] = xs[kSeg * (k >> 5) + (k & 31)];
     }
   } else if constexpr (DUMP) {
     if (a.du && nb == 0 && j == 0 && live)
@@ -318,7 +327,7 @@ __global__ __launch_bounds__(256) void k_dec_down(const SlotRef* pre, const Slot
   constexpr int G = group_of<FMT>();
   constexpr int HPT = (KMAX * I / 8 + 255) / 256;  // 16-byte pieces of h per thread
   __shared__ uint16_t ys[KMAX][ROWS];
-  __shared__ __attribute__((aligned(16))) uint16_t hs[KMAX * I];
+  __shared__ __attribute__((aligned(16))) uint16_t hs[KMAX * (I / 32) * kSeg];
 
   const int nblk = H / ROWS;
   const int mb = blockIdx.x % nblk, t = blockIdx.x / nblk;
@@ -371,7 +380,7 @@ __global__ __launch_bounds__(256) void k_dec_down(const SlotRef* pre, const Slot
     const bool ok = __builtin_amdgcn_readfirstlane(sr.ok) != 0;
     bf16x2 hp[CPL][16];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) unpack16_lds(hs + j * I + 32 * (li + LPR * i), hp[i]);
+    for (int i = 0; i < CPL; ++i) unpack16_lds(hs + kSeg * (j * (I / 32) + li + LPR * i), hp[i]);
     double p[NS];
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
@@ -398,7 +407,10 @@ __global__ __launch_bounds__(256) void k_dec_down(const SlotRef* pre, const Slot
   // waited for here), then the first slot's rows
 #pragma unroll
   for (int u = 0; u < HPT; ++u)
-    if (tid + 256 * u < npc) *(uint4*)(hs + 8 * (tid + 256 * u)) = hv[u];
+    if (tid + 256 * u < npc) {
+      const int pc = tid + 256 * u;  // piece pc & 3 of segment pc >> 2 (I is a multiple of 32)
+      *(uint4*)(hs + kSeg * (pc >> 2) + 8 * (pc & 3)) = hv[u];
+    }
   lds_barrier();
   if (wave < K) finish(wave, sr0, wv, sv);
   // 3. slots 4..k-1 (k > 4), one more per wave
