@@ -968,7 +968,7 @@ __device__ __forceinline__ double row_rscale(double ss, int H, float eps, double
   ss = seg_finish<32, double>(ss, lane);
   if (lane == 0) red[wave] = ss;
   __syncthreads();
-  return 1.0 / sqrt((red[0] + red[1] + red[2] + red[3]) / (double)H + (double)eps);
+  return rsqrt_f64((red[0] + red[1] + red[2] + red[3]) / (double)H + (double)eps);
 }
 
 template <bool NORM, bool Q>

@@ -253,7 +253,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const SlotRef* pre, SlotRef*
     ss = seg_finish<32, double>(ss, lane);
     if (lane == 0) red[wave] = ss;
     __syncthreads();
-    const double rs = 1.0 / sqrt((red[0] + red[1] + red[2] + red[3]) / (double)H + (double)a.eps);
+    const double rs = rsqrt_f64((red[0] + red[1] + red[2] + red[3]) / (double)H + (double)a.eps);
     // each thread rescales the pieces it holds in registers and stores them once
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {

@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ x,
     ss = seg_finish<32, double>(ss, lane);
     if (lane == 0) red[wave] = ss;
     __syncthreads();
-    const double rs = 1.0 / sqrt((red[0] + red[1] + red[2] + red[3]) / (double)H + (double)eps);
+    const double rs = rsqrt_f64((red[0] + red[1] + red[2] + red[3]) / (double)H + (double)eps);
     if (xpiece) {  // rescaled from the registers, stored once
       uint32_t o4[4];
 #pragma unroll
