@@ -325,9 +325,11 @@ __global__ __launch_bounds__(256) void k_dec_down(const SlotRef* pre, const Slot
   using M = typename D::M;
   constexpr int LPR = M::LPR, CPL = M::CPL, RPS = M::RPS, NS = D::NS, ROWS = D::ROWS;
   constexpr int G = group_of<FMT>();
-  constexpr int HPT = (KMAX * I / 8 + 255) / 256;  // 16-byte pieces of h per thread
+  constexpr int HPW = (I / 8 + 63) / 64;  // 16-byte pieces of one slot's h per lane
   __shared__ uint16_t ys[KMAX][ROWS];
-  __shared__ __attribute__((aligned(16))) uint16_t hs[KMAX * (I / 32) * kSeg];
+  // each wave stages the h of its own slot in its own region: no workgroup
+  // barrier stands between a wave's loads and its dot products
+  __shared__ __attribute__((aligned(16))) uint16_t hs[4][(I / 32) * kSeg];
 
   const int nblk = H / ROWS;
   const int mb = blockIdx.x % nblk, t = blockIdx.x / nblk;
@@ -349,11 +351,24 @@ __global__ __launch_bounds__(256) void k_dec_down(const SlotRef* pre, const Slot
   for (int j = 0; j < KMAX; ++j) rwv[j] = rw[t * K + min(j, K - 1)];
   // (without a residual the load reads a harmless valid address, unused)
   const uint16_t resv = *(residual ? residual + (size_t)t * H + m0 + tid % ROWS : rw);
-  const int npc = K * I / 8;
-  const uint16_t* ht = hbuf + (size_t)t * K * I;
-  uint4 hv[HPT];
+  auto load_h = [&](int j, uint4 (&hv)[HPW]) {
+    const uint16_t* hj = hbuf + ((size_t)t * K + j) * I;
 #pragma unroll
-  for (int u = 0; u < HPT; ++u) hv[u] = ldg16(ht + 8 * min(tid + 256 * u, npc - 1));
+    for (int u = 0; u < HPW; ++u) hv[u] = ldg16(hj + 8 * min(lane + 64 * u, I / 8 - 1));
+  };
+  // piece pc & 3 of segment pc >> 2 (I is a multiple of 32); the lanes of
+  // the wave read what the others wrote only after the wave's LDS writes,
+  // which LDS performs in order
+  auto stage_h = [&](const uint4 (&hv)[HPW]) {
+#pragma unroll
+    for (int u = 0; u < HPW; ++u) {
+      const int pc = lane + 64 * u;
+      if (pc < I / 8) *(uint4*)(&hs[wave][0] + kSeg * (pc >> 2) + 8 * (pc & 3)) = hv[u];
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+  uint4 hv[HPW];
+  load_h(j0, hv);
 
   // scales and weights of slot j (a rejected slot reads a harmless valid
   // address, the slot table)
@@ -380,7 +395,7 @@ __global__ __launch_bounds__(256) void k_dec_down(const SlotRef* pre, const Slot
     const bool ok = __builtin_amdgcn_readfirstlane(sr.ok) != 0;
     bf16x2 hp[CPL][16];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) unpack16_lds(hs + kSeg * (j * (I / 32) + li + LPR * i), hp[i]);
+    for (int i = 0; i < CPL; ++i) unpack16_lds(&hs[wave][0] + kSeg * (li + LPR * i), hp[i]);
     double p[NS];
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
@@ -403,21 +418,17 @@ __global__ __launch_bounds__(256) void k_dec_down(const SlotRef* pre, const Slot
   uint32_t sv[NS][CPL];
   issue(sr0, wv, sv);
   __builtin_amdgcn_sched_barrier(0);
-  // 2. h into LDS (its loads are older than the weights, so only they are
-  // waited for here), then the first slot's rows
-#pragma unroll
-  for (int u = 0; u < HPT; ++u)
-    if (tid + 256 * u < npc) {
-      const int pc = tid + 256 * u;  // piece pc & 3 of segment pc >> 2 (I is a multiple of 32)
-      *(uint4*)(hs + kSeg * (pc >> 2) + 8 * (pc & 3)) = hv[u];
-    }
-  lds_barrier();
+  // 2. the slot's h into the wave's LDS region (its loads are older than the
+  // weights, so only they are waited for here), then the slot's rows
+  stage_h(hv);
   if (wave < K) finish(wave, sr0, wv, sv);
   // 3. slots 4..k-1 (k > 4), one more per wave
   if constexpr (KMAX > 4) {
     for (int j = wave + 4; j < K; j += 4) {
       const SlotRef sr = load_slot(slots + t * K + j);
+      load_h(j, hv);
       issue(sr, wv, sv);
+      stage_h(hv);
       finish(j, sr, wv, sv);
     }
   }
