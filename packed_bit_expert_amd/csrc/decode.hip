@@ -189,6 +189,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const SlotRef* pre, SlotRef*
   // one the load reads the workspace table, a harmless valid address, and
   // the slot is resolved below), then the activations, so that both are in
   // flight together
+  if constexpr (PRENORM) __builtin_amdgcn_s_setprio(2);  // the pre-norm chain first
   SlotRef sr = load_slot(pre ? pre + sjc : slots_ws);
   __builtin_amdgcn_sched_barrier(0);
   const uint16_t* xt = x + (size_t)t * H;
@@ -262,6 +263,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const SlotRef* pre, SlotRef*
       *(uint4*)(xs + kSeg * (k8 >> 2) + 8 * (k8 & 3)) = scale8_bf16(xraw[u], rs);
     }
     __syncthreads();
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int i = 0; i < CPL; ++i) unpack16_lds(xs + kSeg * (li + LPR * i), xp[i]);
     if constexpr (DUMP) {
