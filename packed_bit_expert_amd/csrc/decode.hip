@@ -189,7 +189,10 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const SlotRef* pre, SlotRef*
   // one the load reads the workspace table, a harmless valid address, and
   // the slot is resolved below), then the activations, so that both are in
   // flight together
-  if constexpr (PRENORM) __builtin_amdgcn_s_setprio(2);  // the pre-norm chain first
+  // the pre-norm chain first, from the slot load on (raised after it, the
+  // compiler reads the slot through the scalar cache instead, and the step
+  // measured 0.8% slower)
+  if constexpr (PRENORM) __builtin_amdgcn_s_setprio(2);
   SlotRef sr = load_slot(pre ? pre + sjc : slots_ws);
   __builtin_amdgcn_sched_barrier(0);
   const uint16_t* xt = x + (size_t)t * H;
