@@ -128,27 +128,15 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ x,
   if (!PRENORM && xpiece) *(uint4*)(us + 8 * tid) = xv;
 
   if (PRENORM) {  // FP64, once per workgroup, the same order as the layer's gate/up kernel
-    double ss = 0.0;
-    const uint32_t w4[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const double lo = __uint_as_float(w4[q] << 16), hi = __uint_as_float(w4[q] & 0xFFFF0000u);
-      ss += lo * lo + hi * hi;
-    }
+    double ss = sumsq8_bf16(xv);
     ss = seg_finish<32, double>(ss, lane);
     if (lane == 0) red[wave] = ss;
     __syncthreads();
     const double rs = rsqrt_f64((red[0] + red[1] + red[2] + red[3]) / (double)H + (double)eps);
-    if (xpiece) {  // rescaled from the registers, stored once
-      uint32_t o4[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = f64_to_bf16((double)__uint_as_float(w4[q] << 16) * rs);
-        const uint32_t hi = f64_to_bf16((double)__uint_as_float(w4[q] & 0xFFFF0000u) * rs);
-        o4[q] = lo | (hi << 16);
-      }
-      *(uint4*)(us + 8 * tid) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
-    }
+    // rescaled from the registers (the FP32 path with its exact-rounding
+    // guard, as in the layer's kernels), stored once
+    const uint4 uv = scale8_bf16(xv, rs);
+    if (xpiece) *(uint4*)(us + 8 * tid) = uv;
   }
   __syncthreads();
 
