@@ -60,6 +60,10 @@ struct DnShape {
   static constexpr int NS = M::RPS >= 8 ? 1 : 8 / M::RPS;
   static constexpr int ROWS = NS * M::RPS;
   static_assert(NS <= M::LPR && (NS & (NS - 1)) == 0, "load sets per wave");
+  // waves per slot: where a slot's rows take two load sets, two waves share
+  // them (one set each), so that two waves per SIMD overlap their streams
+  static constexpr int SPW = NS >= 2 ? 2 : 1;
+  static constexpr int NSW = NS / SPW;  // load sets per wave
 };
 
 template <int FMT>
@@ -323,24 +327,26 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const SlotRef* pre, SlotRef*
 // Leading arguments as in k_dec_gateup (preloaded into SGPRs).  KMAX (4 or
 // 8) bounds k, so that at top-4 no load or LDS slot is spent on slots 5..8.
 template <int H, int I, int FMT, bool DUMP, int KMAX>
-__global__ __launch_bounds__(256) void k_dec_down(const SlotRef* pre, const SlotRef* slots_ws,
+__global__ __launch_bounds__(256 * DnShape<I>::SPW) void k_dec_down(const SlotRef* pre, const SlotRef* slots_ws,
                                                   const uint16_t* rw, const uint16_t* hbuf,
                                                   const uint16_t* residual, int K, DecodeArgs a) {
   using D = DnShape<I>;
   using M = typename D::M;
-  constexpr int LPR = M::LPR, CPL = M::CPL, RPS = M::RPS, NS = D::NS, ROWS = D::ROWS;
+  constexpr int LPR = M::LPR, CPL = M::CPL, RPS = M::RPS, ROWS = D::ROWS;
+  constexpr int SPW = D::SPW, NS = D::NSW;  // this wave's load sets
   constexpr int G = group_of<FMT>();
   constexpr int HPW = (I / 8 + 63) / 64;  // 16-byte pieces of one slot's h per lane
   __shared__ uint16_t ys[KMAX][ROWS];
   // each wave stages the h of its own slot in its own region: no workgroup
   // barrier stands between a wave's loads and its dot products
-  __shared__ __attribute__((aligned(16))) uint16_t hs[4][(I / 32) * kSeg];
+  __shared__ __attribute__((aligned(16))) uint16_t hs[4 * SPW][(I / 32) * kSeg];
 
   const int nblk = H / ROWS;
   const int mb = blockIdx.x % nblk, t = blockIdx.x / nblk;
   const int m0 = mb * ROWS;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // a scalar: the slot indices
+  const int js = wave % 4, r0 = (wave / 4) * NS * RPS;  // the wave's slot and first row
   const int li = lane % LPR, q = lane / LPR;
   const SlotRef* slots = pre ? pre : slots_ws;
 
@@ -349,7 +355,7 @@ __global__ __launch_bounds__(256) void k_dec_down(const SlotRef* pre, const Slot
   // weights.  Everything is unconditional with clamped indices, so the loads
   // go out back to back and each value is waited for only where it is used.
   // A wave without a slot (k < 4) works on the last one and discards it.
-  const int j0 = min(wave, K - 1);
+  const int j0 = min(js, K - 1);
   const SlotRef sr0 = load_slot(slots + t * K + j0);
   uint16_t rwv[KMAX];
 #pragma unroll
@@ -386,13 +392,13 @@ __global__ __launch_bounds__(256) void k_dec_down(const SlotRef* pre, const Slot
     for (int st = 0; st < NS; ++st)
 #pragma unroll
       for (int i = 0; i < CPL; ++i)
-        sv[st][i] = load_chunk_scale<FMT>(sd + (size_t)(m0 + st * RPS + q) * row_sc,
+        sv[st][i] = load_chunk_scale<FMT>(sd + (size_t)(m0 + r0 + st * RPS + q) * row_sc,
                                           ok ? li + LPR * i : 0);
 #pragma unroll
     for (int st = 0; st < NS; ++st)
 #pragma unroll
       for (int i = 0; i < CPL; ++i)
-        wv[st][i] = ldg16(wd + (size_t)(m0 + st * RPS + q) * row_nib + (ok ? 16 * (li + LPR * i) : 0));
+        wv[st][i] = ldg16(wd + (size_t)(m0 + r0 + st * RPS + q) * row_nib + (ok ? 16 * (li + LPR * i) : 0));
   };
   // y rows of slot j into ys (the dot products, one butterfly over LPR lanes)
   auto finish = [&](int j, const SlotRef& sr, const uint4 (&wv)[NS][CPL],
@@ -410,7 +416,7 @@ __global__ __launch_bounds__(256) void k_dec_down(const SlotRef* pre, const Slot
     }
     const double tot = seg_reduce<NS, LPR>(p, lane);
     if ((li % (LPR / NS)) == 0) {
-      const int r = (li / (LPR / NS)) * RPS + q;
+      const int r = r0 + (li / (LPR / NS)) * RPS + q;
       const uint16_t y = ok ? f64_to_bf16(tot * (double)sr.td) : (uint16_t)0;
       ys[j][r] = y;
       if constexpr (DUMP) {
@@ -426,10 +432,10 @@ __global__ __launch_bounds__(256) void k_dec_down(const SlotRef* pre, const Slot
   // 2. the slot's h into the wave's LDS region (its loads are older than the
   // weights, so only they are waited for here), then the slot's rows
   stage_h(hv);
-  if (wave < K) finish(wave, sr0, wv, sv);
+  if (js < K) finish(js, sr0, wv, sv);
   // 3. slots 4..k-1 (k > 4), one more per wave
   if constexpr (KMAX > 4) {
-    for (int j = wave + 4; j < K; j += 4) {
+    for (int j = js + 4; j < K; j += 4) {
       const SlotRef sr = load_slot(slots + t * K + j);
       load_h(j, hv);
       issue(sr, wv, sv);
@@ -467,10 +473,10 @@ hipError_t launch_variant(const DecodeArgs& a0, hipStream_t s) {
   if (e != hipSuccess) return e;
   if (a.K <= 4)
     return launch_kernel(MOE_KERNEL_DECODE_DOWN, k_dec_down<H, I, FMT, DUMP, 4>,
-                         dim3(a.T * (H / DnShape<I>::ROWS)), dim3(256), 0, s, a.pre,
+                         dim3(a.T * (H / DnShape<I>::ROWS)), dim3(256 * DnShape<I>::SPW), 0, s, a.pre,
                          (const SlotRef*)a.slots, a.rw, (const uint16_t*)a.hbuf, a.residual, a.K, a);
   return launch_kernel(MOE_KERNEL_DECODE_DOWN, k_dec_down<H, I, FMT, DUMP, 8>,
-                       dim3(a.T * (H / DnShape<I>::ROWS)), dim3(256), 0, s, a.pre,
+                       dim3(a.T * (H / DnShape<I>::ROWS)), dim3(256 * DnShape<I>::SPW), 0, s, a.pre,
                        (const SlotRef*)a.slots, a.rw, (const uint16_t*)a.hbuf, a.residual, a.K, a);
 }
 
