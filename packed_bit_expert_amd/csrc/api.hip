@@ -572,17 +572,31 @@ int check_route(const moe_w4a16_cfg* c, const void* x, const void* router_w,
   return MOE_OK;
 }
 
+// With k (the layer the ids are for) on the decode path, the router also
+// resolves the slots it selects into the workspace's slot table, which is
+// returned through pre for the layer's kernels.
 int run_route(const moe_w4a16_cfg* c, const void* x, const void* router_w, const float* bias,
-              int32_t* ids, void* rw) {
+              int32_t* ids, void* rw, const Call* k = nullptr, const SlotRef** pre = nullptr) {
   const int T = c->num_tokens;
+  if (pre) *pre = nullptr;
   if (T == 0) return ok();
   const Layout L = layout(T, c->hidden, c->inter, c->num_experts, c->top_k);
+  uint8_t* ws = (uint8_t*)c->workspace;
+  RouteResolve res;
+  if (k && pre && use_decode(c) && !(c->flags & MOE_FLAG_SERIAL)) {
+    res.wtab = (const uint8_t* const*)k->wtab;
+    res.stab = (const uint8_t* const*)k->stab;
+    res.tsc = k->tsc;
+    res.flags = c->flags;
+    res.err = &((Ctrl*)ws)->err;
+    res.slots = (SlotRef*)(ws + L.slots);
+  }
   const hipError_t e = launch_route(
       (const uint16_t*)x, (const uint16_t*)router_w, bias, T, c->hidden, c->num_experts, c->top_k,
-      (c->flags & MOE_FLAG_PRENORM) != 0, c->prenorm_eps,
-      (double*)((uint8_t*)c->workspace + L.logits), (uint32_t*)((uint8_t*)c->workspace + kRouterCountOff),
-      ids, (uint16_t*)rw, (hipStream_t)c->stream);
+      (c->flags & MOE_FLAG_PRENORM) != 0, c->prenorm_eps, (double*)(ws + L.logits),
+      (uint32_t*)(ws + kRouterCountOff), ids, (uint16_t*)rw, res, (hipStream_t)c->stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");
+  if (res.slots) *pre = res.slots;
   return ok();
 }
 
@@ -606,9 +620,10 @@ extern "C" int moe_w4a16_forward_routed(const void* x, const void* router_w,
          nullptr};
   rc = check_call(cfg, k);
   if (rc) return rc;
-  rc = run_route(cfg, x, router_w, expert_bias, expert_ids, route_w);
+  const SlotRef* pre = nullptr;
+  rc = run_route(cfg, x, router_w, expert_bias, expert_ids, route_w, &k, &pre);
   if (rc) return rc;
-  return run_layer(cfg, k);
+  return run_layer(cfg, k, pre);
 }
 
 extern "C" int moe_w4a16_stack_forward_routed(int32_t num_layers, const void* x,
@@ -638,17 +653,18 @@ extern "C" int moe_w4a16_stack_forward_routed(int32_t num_layers, const void* x,
     void* dst = ((num_layers - 1 - l) % 2 == 0) ? out : ping;
     int32_t* ids_l = expert_ids + (size_t)l * T * K;
     void* rw_l = (uint16_t*)route_w + (size_t)l * T * K;
-    rc = run_route(&lc, src, (const uint16_t*)router_w + (size_t)l * E * H,
-                   expert_bias ? expert_bias + (size_t)l * E : nullptr, ids_l, rw_l);
-    if (rc) return rc;
     lc.residual = src;
     lc.tensor_scales = tensor_scales ? tensor_scales + (size_t)l * E * 2 : nullptr;
     Call kl{src, ids_l, rw_l, packed_weights + (size_t)l * E, scales + (size_t)l * E,
             lc.tensor_scales, src, dst, nullptr};
+    const SlotRef* pre = nullptr;
+    rc = run_route(&lc, src, (const uint16_t*)router_w + (size_t)l * E * H,
+                   expert_bias ? expert_bias + (size_t)l * E : nullptr, ids_l, rw_l, &kl, &pre);
+    if (rc) return rc;
     const bool batched = !use_decode(&lc);
     kl.x_normed = batched && l > 0;
     kl.norm_out = batched && l + 1 < num_layers;
-    rc = run_layer(&lc, kl);
+    rc = run_layer(&lc, kl, pre);
     if (rc) return rc;
     src = dst;
   }

@@ -119,9 +119,22 @@ hipError_t launch_read_burst(const void* src, size_t bytes, int loads_per_lane, 
 bool router_supported(int H, int E, int K);
 // logits [T][E] FP64 and count [T] (zero, left zero) workspace; ids [T][K];
 // rw [T][K] BF16
+// With slots set, the router also resolves the slots it selects (expert
+// bases, tensor scales, base alignment under MOE_FLAG_CHECK_IDS) into the
+// table the decode kernels read, so their first dependent load is the table
+// entry, not the id and then the expert tables.
+struct RouteResolve {
+  const uint8_t* const* wtab = nullptr;
+  const uint8_t* const* stab = nullptr;
+  const float* tsc = nullptr;
+  uint32_t flags = 0;
+  int* err = nullptr;
+  SlotRef* slots = nullptr;  // [T][K], or null: no resolution
+};
+
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H,
                         int E, int K, bool prenorm, float eps, double* logits, uint32_t* count,
-                        int32_t* ids, uint16_t* rw, hipStream_t s);
+                        int32_t* ids, uint16_t* rw, const RouteResolve& res, hipStream_t s);
 
 // Kernel timing (moe_w4a16_timing_*): while the calling thread times
 // launches, each launch gets a start and a stop event that the dispatch

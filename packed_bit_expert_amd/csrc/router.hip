@@ -24,7 +24,7 @@ namespace {
 // One wave: the k-of-E selection of token t from its FP64 logits.
 // Lane l holds experts l, l + 64, l + 128, l + 192 (E <= 256).
 __device__ void router_select(const double* logits, const float* bias, int E, int K, int lane,
-                              int32_t* ids, uint16_t* rw) {
+                              int32_t* ids, uint16_t* rw, const RouteResolve& res) {
   double s[4], c[4];
   bool taken[4];
   double l[4];
@@ -38,6 +38,26 @@ __device__ void router_select(const double* logits, const float* bias, int E, in
     l[i] = __hip_atomic_load(logits + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     bv[i] = bsrc[e];
   }
+  // with a slot table to fill, every expert's table entries are loaded now,
+  // next to the logits, so that the winners' entries are at hand (a lane
+  // holds those of its experts) instead of a round trip after the selection
+  uint64_t tw[4] = {0, 0, 0, 0}, ts[4] = {0, 0, 0, 0};
+  float tg[4] = {1.f, 1.f, 1.f, 1.f}, td[4] = {1.f, 1.f, 1.f, 1.f};
+  if (res.slots) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (64 * i >= E) break;
+      const int e = lane + 64 * i < E ? lane + 64 * i : 0;
+      tw[i] = (uint64_t)res.wtab[e];
+      ts[i] = (uint64_t)res.stab[e];
+      if (res.tsc) {
+        tg[i] = res.tsc[2 * e];
+        td[i] = res.tsc[2 * e + 1];
+      }
+    }
+  }
+  uint64_t my_w = 0, my_sb = 0;  // lane j: slot j's expert bases and tensor scales
+  float my_tg = 1.f, my_td = 1.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
@@ -84,11 +104,55 @@ __device__ void router_select(const double* logits, const float* bias, int E, in
       my_s = bs;
       my_e = (int32_t)be;
     }
+    if (res.slots) {  // the winner's entries, from the lane that holds them
+      // (be is the same in every lane after the butterfly)
+      const int src = __builtin_amdgcn_readfirstlane((int)(be & 63u));
+      const int reg = __builtin_amdgcn_readfirstlane((int)(be >> 6));
+      uint64_t w = tw[0], sb = ts[0];
+      float g = tg[0], d = td[0];
+#pragma unroll
+      for (int i = 1; i < 4; ++i)
+        if (reg == i) {
+          w = tw[i];
+          sb = ts[i];
+          g = tg[i];
+          d = td[i];
+        }
+      const uint64_t ww = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(w >> 32), src) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)w, src);
+      const uint64_t ss = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(sb >> 32), src) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)sb, src);
+      const float gg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), src));
+      const float dd = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), src));
+      if (lane == j) {
+        my_w = ww;
+        my_sb = ss;
+        my_tg = gg;
+        my_td = dd;
+      }
+    }
     sum += bs;  // slot order, as the oracle sums
   }
   if (lane < K) {
     ids[lane] = my_e;
     rw[lane] = f64_to_bf16(my_s / sum);
+    if (res.slots) {
+      // the ids are in range by construction; under MOE_FLAG_CHECK_IDS a
+      // misaligned expert base rejects the slot, as the decode kernels do
+      SlotRef r;
+      r.w = (const uint8_t*)my_w;
+      r.s = (const uint8_t*)my_sb;
+      r.tg = my_tg;
+      r.td = my_td;
+      r.ok = 1;
+      r.pad = 0;
+      if ((res.flags & MOE_FLAG_CHECK_IDS) && ((my_w | my_sb) & 15u)) {
+        if (res.err) atomicOr(res.err, kErrAlign);
+        r.tg = r.td = 1.f;
+        r.ok = 0;
+      }
+      res.slots[lane] = r;
+    }
   }
 }
 
@@ -108,7 +172,7 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ x,
                                                 const float* __restrict__ bias, int H, int E,
                                                 int K, float eps, double* logits, uint32_t* count,
                                                 int32_t* __restrict__ ids,
-                                                uint16_t* __restrict__ rw) {
+                                                uint16_t* __restrict__ rw, RouteResolve res) {
   // every argument fetched in one scalar batch
   asm volatile("" ::"s"(x), "s"(wr), "s"(bias), "s"(H), "s"(E), "s"(K), "s"(eps), "s"(logits),
                "s"(count), "s"(ids), "s"(rw));
@@ -179,7 +243,10 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ x,
   __syncthreads();
   if (!last || wave != 0) return;
   // router_select reads the logits with device-coherent loads
-  router_select(logits + (size_t)t * E, bias, E, K, lane, ids + (size_t)t * K, rw + (size_t)t * K);
+  RouteResolve rt = res;
+  if (rt.slots) rt.slots += (size_t)t * K;
+  router_select(logits + (size_t)t * E, bias, E, K, lane, ids + (size_t)t * K, rw + (size_t)t * K,
+                rt);
 }
 
 }  // namespace
@@ -190,7 +257,7 @@ bool router_supported(int H, int E, int K) {
 
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H,
                         int E, int K, bool prenorm, float eps, double* logits, uint32_t* count,
-                        int32_t* ids, uint16_t* rw, hipStream_t s) {
+                        int32_t* ids, uint16_t* rw, const RouteResolve& res, hipStream_t s) {
   // at most kRouterCounters tokens per launch: their counters sit at a fixed
   // place of the workspace, so a workspace reused with another cfg still
   // finds them at zero; launches on one stream run one after the other
@@ -201,11 +268,13 @@ hipError_t launch_route(const uint16_t* x, const uint16_t* wr, const float* bias
     double* lc = logits + (size_t)t0 * E;
     int32_t* ic = ids + (size_t)t0 * K;
     uint16_t* rc = rw + (size_t)t0 * K;
+    RouteResolve rs = res;
+    if (rs.slots) rs.slots += (size_t)t0 * K;
     const hipError_t e =
         prenorm ? launch_kernel(MOE_KERNEL_ROUTER, k_router<true>, grid, dim3(256), 0, s, xc, wr,
-                                bias, H, E, K, eps, lc, count, ic, rc)
+                                bias, H, E, K, eps, lc, count, ic, rc, rs)
                 : launch_kernel(MOE_KERNEL_ROUTER, k_router<false>, grid, dim3(256), 0, s, xc, wr,
-                                bias, H, E, K, eps, lc, count, ic, rc);
+                                bias, H, E, K, eps, lc, count, ic, rc, rs);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
