@@ -283,6 +283,24 @@ def test_decode_top_k_other_than_four(K, T, flags):
     GH.compare(out, ref, f"k={K} out")
 
 
+@pytest.mark.parametrize("K,flags", [(2, 0), (6, M.FLAG_PRENORM), (8, 0)])
+def test_decode_top_k_other_than_four_full_shape(layer_mx, K, flags):
+    """The same at the LFM2.5-24B-A2B shape, where two down waves share each
+    slot's rows (one load set each) and the top-8 build gives each of them a
+    second slot."""
+    banner(f"decode top_k={K} H={LFM.hidden} T=1 flags={flags}")
+    x = S.activations(11, 0, 1, 1, LFM.hidden)
+    ids, rw = S.routing_uniform(11, 0, 1, 1, LFM.experts, K)
+    r = S.activations(12, 0, 1, 1, LFM.hidden)
+    out, d, st = layer_mx.gpu(x, ids, rw, residual=r, flags=flags, dumps=True)
+    assert st == 0
+    ref, rd = layer_mx.oracle(x, ids, rw, residual=r, prenorm=bool(flags & M.FLAG_PRENORM),
+                              dumps=True)
+    for k in ("h", "y"):
+        GH.compare(d[k], rd[k], f"k={K} {k}")
+    GH.compare(out, ref, f"k={K} out")
+
+
 def test_prenorm_residual_decode(layer_mx):
     banner("pre-norm + residual, T=1 decode and T=3 batched")
     for T in (1, 3):

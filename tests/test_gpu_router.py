@@ -240,6 +240,42 @@ def test_routed_stack_w4a4(routed_stack):
     assert (layers, tokens) == (4, 4 * T)
 
 
+@pytest.mark.parametrize("misaligned", [False, True])
+def test_routed_decode_slot_resolution_checks(routed_stack, misaligned):
+    """On the decode path the router resolves the slots it selects for the
+    layer's kernels.  Under MOE_FLAG_CHECK_IDS a misaligned expert base is
+    rejected there as the decode kernels reject it: every base off by one
+    byte leaves y = 0 in every slot (out = the residual) and the alignment
+    bit in the status word; the same call with aligned bases reports 0."""
+    st, wr, b, wrd, bd = routed_stack
+    banner(f"routed decode, CHECK_IDS, misaligned bases = {misaligned}")
+    x = S.activations(FAMILY, 0, 0, 1, LFM.hidden)
+    wt, stb, _ = st.layer_tables(0)
+    if misaligned:
+        wt = wt + 1
+    hd = GH.bf16_dev(x)
+    out = torch.empty_like(hd)
+    ids = torch.empty((1, 4), dtype=torch.int32, device=GH.dev())
+    rw = torch.empty((1, 4), dtype=torch.bfloat16, device=GH.dev())
+    cfg = M.make_cfg(1, flags=M.FLAG_PRENORM | M.FLAG_CHECK_IDS, residual=hd, prenorm_eps=GH.EPS)
+    ws = torch.zeros(M.moe_w4a16_workspace_bytes(cfg), dtype=torch.uint8, device=GH.dev())
+    cfg.workspace, cfg.workspace_bytes = ws.data_ptr(), ws.numel()
+    M.moe_w4a16_forward_routed(hd, wrd[0], bd[0], wt, stb, out, ids, rw, cfg)
+    torch.cuda.synchronize()
+    status = M.moe_w4a16_device_status(ws)
+    if misaligned:
+        assert status == 2, status
+        assert np.array_equal(GH.bits_host(out), x.reshape(1, -1))
+    else:
+        assert status == 0, status
+        rids, rrw, lg = O.route(x, wr[0], b[0], top_k=4, prenorm=True, eps=GH.EPS, logits=True)
+        gids = ids.cpu().numpy()
+        check_ids(gids, rids, lg, b[0], 4)
+        lay = GH.Layer(LFM, S.FMT_E8M0_G32, 0, store=st, l=0)
+        ref = lay.oracle(x, gids, GH.bits_host(rw), residual=x, prenorm=True)
+        GH.compare(GH.bits_host(out), ref, "routed decode with checks")
+
+
 def test_router_coefficients_hand_worked():
     """The hand-worked coefficient case of the oracle's pins on the device:
     logits (0, bf16(ln 3), -2) select experts (1, 0) with coefficients
