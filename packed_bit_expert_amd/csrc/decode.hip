@@ -155,8 +155,9 @@ __global__ __launch_bounds__(256) void k_resolve(const int32_t* ids, const uint8
 }
 
 // Grouped gate/up GEMV + silu(g) * v.  A 256-thread workgroup is four
-// independent waves, each owning RW rows of gate and of up of one (token,
-// slot).  All loads of a wave are issued before any arithmetic; the
+// waves of one (token, slot), each owning RW rows of gate and of up; their
+// row sums meet in LDS at the end, where wave 0 finishes the workgroup's
+// rows.  All loads of a wave are issued before any arithmetic; the
 // activation slices come first because vmcnt retires loads in issue order.
 // With PRENORM the workgroup stages x in LDS and computes the weightless RMS
 // pre-norm once (FP64) for its four waves.  A rejected slot reads a harmless
@@ -320,10 +321,10 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const SlotRef* pre, SlotRef*
   }
 }
 
-// Grouped down GEMV for ROWS output rows of every slot (one wave per slot),
-// then the slot-order BF16 combine (+ residual) of those rows.  The token's h
-// (all k slots, k * I BF16) is read once per workgroup into LDS; every lane
-// then takes its slices from there instead of re-reading them from L2.
+// Grouped down GEMV for ROWS output rows of every slot (SPW waves per slot,
+// one load set of rows each), then the slot-order BF16 combine (+ residual)
+// of those rows.  Each wave stages its slot's h (I BF16) in LDS once; every
+// lane then takes its slices from there instead of re-reading them from L2.
 // Leading arguments as in k_dec_gateup (preloaded into SGPRs).  KMAX (4 or
 // 8) bounds k, so that at top-4 no load or LDS slot is spent on slots 5..8.
 template <int H, int I, int FMT, bool DUMP, int KMAX>
