@@ -312,6 +312,33 @@ def test_prenorm_residual_decode(layer_mx):
         GH.compare(out, ref, "out")
 
 
+@pytest.mark.parametrize("path", [M.FLAG_FORCE_DECODE, M.FLAG_FORCE_BATCHED])
+def test_prenorm_special_values(layer_mx, path):
+    """The pre-norm's FP32 rescale hands values next to a BF16 rounding
+    midpoint, and subnormal products, to FP64: rows with exact zeros and BF16
+    subnormals, a row spanning 2^-60 .. 2^60, and a constant row must give
+    the oracle's u bit for bit on both paths."""
+    banner(f"pre-norm special values, flags={path}")
+    rng = np.random.default_rng(21)
+    H = LFM.hidden
+    rows = rng.standard_normal((3, H)).astype(np.float32)
+    rows[1] *= np.exp2(rng.integers(-60, 61, size=H)).astype(np.float32)
+    x = S.to_bf16_bits(rows)
+    idx = rng.permutation(H)
+    x[0, idx[:64]] = 0                                                    # exact zeros
+    sub = rng.integers(1, 128, size=64).astype(np.uint16)                 # BF16 subnormals
+    x[0, idx[64:128]] = sub | (rng.integers(0, 2, size=64).astype(np.uint16) << 15)
+    x[2] = S.to_bf16_bits(np.full(H, 3.0, np.float32))                    # constant row
+    ids, rw = S.routing_uniform(13, 0, 3, 3, LFM.experts, 4)
+    out, d, st = layer_mx.gpu(x, ids, rw, residual=x, flags=M.FLAG_PRENORM | path, dumps=True)
+    ref, rd = layer_mx.oracle(x, ids, rw, residual=x, prenorm=True, dumps=True)
+    assert st == 0
+    assert np.array_equal(d["u"], rd["u"]), f"{int(np.sum(d['u'] != rd['u']))} u values differ"
+    for k in ("h", "y"):
+        GH.compare(d[k], rd[k], f"special {k}")
+    GH.compare(out, ref, "special out")
+
+
 def test_determinism_and_zero_tokens(layer_mx):
     banner("determinism (3 runs) and T=0")
     x, ids, rw = S.inputs(S.WORKLOADS["c2"], 0, 3)
