@@ -144,7 +144,7 @@ def decode_floor(args, store, stream, dev, xs, ids, rws, cfg, warmup, steps, buf
         return float(np.mean(ts) * 1e3)
 
     empty = {"1": timed(lambda i: M.moe_w4a16_empty_launch(768, 256, sink, stream)),
-             "2": timed(lambda i: M.moe_w4a16_empty_launch(256, 256, sink, stream))}
+             "2": timed(lambda i: M.moe_w4a16_empty_launch(256, 512, sink, stream))}
 
     # the same two floors inside a captured graph, as the step itself runs:
     # the decode launches of a step with no arithmetic, and as many empty
@@ -171,10 +171,10 @@ def decode_floor(args, store, stream, dev, xs, ids, rws, cfg, warmup, steps, buf
         steps)
 
     def empty_step(r):
-        M.moe_w4a16_empty_launch(256, 64, sink, stream)  # the slot resolve's place
+        M.moe_w4a16_empty_launch(1, 256, sink, stream)  # the slot resolve's place
         for _ in range(L):
             M.moe_w4a16_empty_launch(768, 256, sink, stream)
-            M.moe_w4a16_empty_launch(256, 256, sink, stream)
+            M.moe_w4a16_empty_launch(256, 512, sink, stream)
 
     empty_step_ms = graph_ms(empty_step, steps)
 

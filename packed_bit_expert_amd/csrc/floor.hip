@@ -61,46 +61,40 @@ __global__ __launch_bounds__(256) void k_floor_gateup(const SlotRef* pre, const 
   if (li == 0 && (q & 1) == 0) hbuf[(size_t)sj * kI + n] = (uint16_t)acc;
 }
 
-// Down: 256 workgroups of 8 output rows, wave j = slot j; the workgroup loads
-// the token's h (k * I BF16, 16 bytes per thread three times), every thread
-// the 8 coefficients and one residual value; lane (li, q) loads the scale
-// byte and 16-byte chunk of rows m0 + q and m0 + 4 + q for chunks li,
-// li + 16, li + 32.
-__global__ __launch_bounds__(256) void k_floor_down(const SlotRef* pre, const uint16_t* hbuf,
+// Down: 256 workgroups of 8 output rows and 8 waves; wave w takes slot
+// w % 4 and the 4 rows m0 + 4 (w / 4) + q (one load set), loads that slot's
+// h (I BF16, 16 bytes per lane three times), the 4 coefficients and one
+// residual value; lane (li, q) loads the scale byte and 16-byte chunk of
+// its row for chunks li, li + 16, li + 32.
+__global__ __launch_bounds__(512) void k_floor_down(const SlotRef* pre, const uint16_t* hbuf,
                                                     const uint16_t* rw, const uint16_t* residual,
                                                     uint16_t* out) {
   asm volatile("" ::"s"(pre), "s"(hbuf), "s"(rw), "s"(residual), "s"(out));
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int js = wave & 3, st = wave >> 2;
   const int m0 = blockIdx.x * 8;
-  const SlotRef sr = load_slot(pre + wave);
+  const SlotRef sr = load_slot(pre + js);
   uint32_t acc = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc ^= rw[j < kK ? j : kK - 1];
+  for (int j = 0; j < kK; ++j) acc ^= rw[j];
   acc ^= residual[m0 + tid % 8];
   uint4 hv[3];
 #pragma unroll
-  for (int u = 0; u < 3; ++u) hv[u] = ldg16(hbuf + 8 * (tid + 256 * u));
+  for (int u = 0; u < 3; ++u) hv[u] = ldg16(hbuf + (size_t)js * kI + 8 * (lane + 64 * u));
   const int li = lane & 15, q = lane >> 4;
+  const int row = m0 + 4 * st + q;
   const uint8_t* wd = sr.w + (size_t)kI * kH;
   const uint8_t* sd = sr.s + 2 * (size_t)kI * (kH / 32);
-  uint32_t sv[2][3];
-  uint4 wv[2][3];
+  uint32_t sv[3];
+  uint4 wv[3];
 #pragma unroll
-  for (int st = 0; st < 2; ++st)
+  for (int i = 0; i < 3; ++i) sv[i] = ldg<uint8_t>(sd + (size_t)row * (kI / 32) + li + 16 * i);
 #pragma unroll
-    for (int i = 0; i < 3; ++i)
-      sv[st][i] = ldg<uint8_t>(sd + (size_t)(m0 + st * 4 + q) * (kI / 32) + li + 16 * i);
-#pragma unroll
-  for (int st = 0; st < 2; ++st)
-#pragma unroll
-    for (int i = 0; i < 3; ++i)
-      wv[st][i] = ldg16(wd + (size_t)(m0 + st * 4 + q) * (kI / 2) + 16 * (li + 16 * i));
+  for (int i = 0; i < 3; ++i) wv[i] = ldg16(wd + (size_t)row * (kI / 2) + 16 * (li + 16 * i));
 #pragma unroll
   for (int u = 0; u < 3; ++u) acc ^= fold(hv[u]);
 #pragma unroll
-  for (int st = 0; st < 2; ++st)
-#pragma unroll
-    for (int i = 0; i < 3; ++i) acc ^= sv[st][i] ^ fold(wv[st][i]);
+  for (int i = 0; i < 3; ++i) acc ^= sv[i] ^ fold(wv[i]);
   // the decode kernel's stores: one output value per row of the workgroup
   if (tid < 8) out[m0 + tid] = (uint16_t)acc;
 }
@@ -176,7 +170,7 @@ hipError_t launch_decode_floor(const SlotRef* pre, const uint16_t* x, uint16_t* 
   hipError_t e = launch_kernel(MOE_KERNEL_FLOOR_GATE_UP, k_floor_gateup, dim3(kK * kI / 2 / 4),
                                dim3(256), 0, s, pre, x, hbuf);
   if (e != hipSuccess) return e;
-  return launch_kernel(MOE_KERNEL_FLOOR_DOWN, k_floor_down, dim3(kH / 8), dim3(256), 0, s, pre,
+  return launch_kernel(MOE_KERNEL_FLOOR_DOWN, k_floor_down, dim3(kH / 8), dim3(512), 0, s, pre,
                        (const uint16_t*)hbuf, rw, residual, out);
 }
 

@@ -56,27 +56,25 @@ def _floor_reference(x, ids, rw, experts):
                 h[sj * I + n] = acc & 0xFFFF
     h16 = h.astype(np.uint16)
     hb = h16.view(np.uint8)
-    nib0, sc0 = experts[int(ids[0])]                             # wave 0 = slot 0
+    nib0, sc0 = experts[int(ids[0])]                             # wave 0: slot 0, rows m0..m0+3
     down_w = nib0[I * H:].reshape(H, I // 2)
     down_s = sc0[2 * I * H // 32:].reshape(H, I // 32)
     rwv = [int(v) for v in rw.reshape(-1)]
     xv = x.reshape(-1)
     out = np.zeros(H, np.uint16)
     for m0 in range(0, H, 8):
-        for tid in range(8):
+        for tid in range(8):                                   # the storing lanes: li = tid, q = 0
             acc = 0
-            for j in range(8):
-                acc ^= rwv[min(j, K - 1)]
+            for j in range(K):
+                acc ^= rwv[j]
             acc ^= int(xv[m0 + tid])
-            for u in range(3):
-                e0 = 8 * (tid + 256 * u)
+            for u in range(3):                                 # slot 0's h, piece tid + 64 u
+                e0 = 8 * (tid + 64 * u)
                 acc ^= int(_fold16(hb[2 * e0: 2 * e0 + 16])[0])
-            for st in range(2):
-                row = m0 + 4 * st
-                for i in range(3):
-                    acc ^= int(down_s[row, tid + 16 * i])
-                    c = 16 * (tid + 16 * i)
-                    acc ^= int(_fold16(down_w[row, c: c + 16])[0])
+            for i in range(3):
+                acc ^= int(down_s[m0, tid + 16 * i])
+                c = 16 * (tid + 16 * i)
+                acc ^= int(_fold16(down_w[m0, c: c + 16])[0])
             out[m0 + tid] = acc & 0xFFFF
     return h16, out
 
